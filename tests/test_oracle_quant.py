@@ -1,0 +1,91 @@
+"""Pins for the oracle's block quantizer and Hadamard rotation.
+
+Pinned by: the absmax definition (the largest element lands on the top code),
+the zero guard, the e4m3 error bound, torch's float8_e4m3fn cast of the same
+float32 quotients (a library routine), SciPy's Hadamard matrix (a library
+routine) and the orthogonality that makes Q K^T invariant.
+"""
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+from oracle import quantize_blocks, dequantize_blocks, hadamard_matrix, hadamard_rotate, e4m3_decode
+
+
+def _x(shape, seed=0):
+    return np.random.default_rng(seed).standard_normal(shape).astype(np.float32)
+
+
+@pytest.mark.parametrize("block", [64, 128])
+@pytest.mark.parametrize("S", [128, 200, 64, 1])
+def test_scale_is_absmax_over_448(block, S):
+    x = _x((2, 3, S, 128))
+    codes, scales = quantize_blocks(x, block)
+    nb = (S + block - 1) // block
+    assert scales.shape == (2, 3, nb) and scales.dtype == np.float32
+    for j in range(nb):
+        blk = x[:, :, j * block:(j + 1) * block]
+        amax = np.abs(blk).max(axis=(2, 3))
+        assert np.array_equal(scales[:, :, j], (amax / np.float32(448.0)).astype(np.float32))
+        # the largest-magnitude element of each block is coded as +-448 (0x7E / 0xFE)
+        for b in range(2):
+            for h in range(3):
+                i = np.unravel_index(np.argmax(np.abs(blk[b, h])), blk[b, h].shape)
+                assert codes[b, h, j * block + i[0], i[1]] & 0x7F == 0x7E
+
+
+def test_zero_block_guard():
+    x = _x((1, 1, 128, 128))
+    x[:, :, :64] = 0.0
+    codes, scales = quantize_blocks(x, 64)
+    assert scales[0, 0, 0] == 1.0
+    assert np.all(codes[0, 0, :64] == 0)
+    assert scales[0, 0, 1] != 1.0
+
+
+def test_dequantization_error_bound():
+    x = _x((1, 2, 256, 128), seed=1)
+    codes, scales = quantize_blocks(x, 128)
+    xd = dequantize_blocks(codes, scales, 128)
+    s = np.repeat(scales.astype(np.float64), 128, axis=2)[..., None]
+    y = np.abs(x / s)
+    err = np.abs(xd - x) / s
+    normal = y >= 2.0 ** -6
+    # 3 mantissa bits: relative error at most 2^-4 (half an ulp) plus the float32 quotient's rounding
+    assert np.all(err[normal] <= y[normal] * (2.0 ** -4) * (1 + 1e-5))
+    # subnormal range: absolute error at most half the subnormal spacing 2^-9
+    assert np.all(err[~normal] <= 2.0 ** -10 * (1 + 1e-5))
+
+
+def test_codes_match_torch_cast_of_quotients():
+    x = _x((1, 4, 192, 128), seed=2) * np.float32(3.0)
+    codes, scales = quantize_blocks(x, 64)
+    s = np.repeat(scales, 64, axis=2)[:, :, :192, None]
+    q = (torch.from_numpy(x) / torch.from_numpy(s)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, q)
+
+
+def test_hadamard_matches_scipy_and_is_orthogonal():
+    for n in [1, 2, 4, 8, 64, 128]:
+        h = hadamard_matrix(n)
+        assert np.array_equal(h, scipy.linalg.hadamard(n))
+        assert np.array_equal(h @ h.T, n * np.eye(n))
+    with pytest.raises(ValueError):
+        hadamard_matrix(96)
+
+
+def test_hadamard_rotation_preserves_scores_and_spreads_outliers():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((64, 128))
+    k = rng.standard_normal((64, 128))
+    q[:, 7] *= 15
+    k[:, 7] *= 15
+    qr, kr = hadamard_rotate(q), hadamard_rotate(k)
+    assert np.allclose(qr @ kr.T, q @ k.T, rtol=0, atol=1e-10)
+    # a single outlier channel is spread evenly over all 128 channels
+    e = np.zeros(128)
+    e[7] = 1.0
+    assert np.allclose(np.abs(hadamard_rotate(e)), 1 / np.sqrt(128))
+    assert np.abs(kr).max() < np.abs(k).max() / 3
