@@ -1,0 +1,246 @@
+"""Benchmark: causal prefill attention TFLOP/s on one MI355X, FP8 (e4m3) and BF16.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa32k] [--no-cpu]
+
+Workload (default ``gqa32k``): B=1, Hq=32, Hkv=8, S=32768, D=128, causal, Q/K/V
+~ N(0, 1) float32 from seed, resident in HBM before timing. One FP8 step is the
+whole hot path: quantize Q, K and V to e4m3 with per-128-token scales, then the
+FP8 attention kernel. One BF16 step is the BF16 attention kernel on bfloat16
+inputs. FLOPs follow the FlashAttention causal convention, 2 (Dqk + Dv) S^2 / 2 per
+(batch, query head); softmax work is not counted.
+
+Prints one JSON line. ``value`` is FP8 whole-step throughput; the attention kernel
+alone is timed with HIP events on the stream it runs on and reported against the
+datasheet dense FP8 peak in ``roofline``; BF16 is reported in ``bf16``. The CPU
+baseline times the fp64 oracle on a bounded sample (one head, a block of query
+rows) on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X datasheet dense peaks (256 CUs x 2.4 GHz, an MFMA issued every cycle), TFLOP/s
+PEAK_FP8 = 5033.2
+PEAK_BF16 = 2516.6
+PEAK_HBM_GBS = 8000.0
+
+KERNEL_SOURCES = ["fp8_causal_prefill_amd/csrc/attn_fwd.hip", "fp8_causal_prefill_amd/csrc/device.h"]
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def hbm_traffic(workload_name, dtype):
+    """Measured HBM bytes per attention launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{dtype}_{workload_name}_hbm.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def time_loop(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def cpu_baseline(w, q, k, v, target_s=15.0):
+    """Time the fp64 oracle (quantize one head's Q/K/V, dequantize, attention) on a
+    bounded sample: the last rows of query head 0, sized for about target_s seconds."""
+    from oracle import causal_attention, dequantize_blocks, quantize_blocks
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    S = w.S
+    hkv = 0
+    qh, kh, vh = q[:1, :1], k[:1, hkv:hkv + 1], v[:1, hkv:hkv + 1]
+    t0 = time.perf_counter()
+    parts = [quantize_blocks(x, w.scale_block) for x in (qh, kh, vh)]
+    deq = [dequantize_blocks(c, s, w.scale_block) for c, s in parts]
+    t_prep = time.perf_counter() - t0
+    # calibrate on a small block of rows, then run the sized sample
+    rows = np.arange(S - 256, S)
+    t1 = time.perf_counter()
+    causal_attention(deq[0], deq[1], deq[2], w.softmax_scale, rows=rows)
+    t_cal = time.perf_counter() - t1
+    n = int(min(S, max(256, 256 * (target_s / max(t_cal, 1e-3)))))
+    n = (n // 256) * 256
+    rows = np.arange(S - n, S)
+    t2 = time.perf_counter()
+    o, _ = causal_attention(deq[0], deq[1], deq[2], w.softmax_scale, rows=rows)
+    t_att = time.perf_counter() - t2
+    flops = 2.0 * (w.Dqk + w.Dv) * float(np.sum(rows + 1))
+    frac_prep = t_prep * (n / S)  # the sample's share of the one-head quantization
+    tflops = flops / (t_att + frac_prep) / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 oracle: quantize+dequantize query head 0 and its KV head, attention for the last "
+                      f"{n} query rows of that head (of {w.B * w.Hq} heads x {S} rows); {t_att:.1f} s",
+            "seconds": round(t_att + frac_prep, 3)}, rows, o, parts
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="gqa32k")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-bf16", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_causal_prefill_amd as zy
+    from workloads import WORKLOADS, generate
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    print(f"[bench] workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} S={w.S} Dqk={w.Dqk} Dv={w.Dv}", file=sys.stderr,
+          flush=True)
+    q, k, v = generate(w, seed=0)
+    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    blk = w.scale_block
+    scale = w.softmax_scale
+    flops = w.flops
+
+    # ---------------- FP8: quantize + attention ----------------
+    qc = torch.empty(qd.shape, dtype=torch.uint8, device=dev)
+    kc = torch.empty(kd.shape, dtype=torch.uint8, device=dev)
+    vc = torch.empty(vd.shape, dtype=torch.uint8, device=dev)
+    nb = (w.S + blk - 1) // blk
+    qs = torch.empty((w.B, w.Hq, nb), dtype=torch.float32, device=dev)
+    ks = torch.empty((w.B, w.Hkv, nb), dtype=torch.float32, device=dev)
+    vs = torch.empty((w.B, w.Hkv, nb), dtype=torch.float32, device=dev)
+    o8 = torch.empty((w.B, w.Hq, w.S, w.Dv), dtype=torch.bfloat16, device=dev)
+
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def fp8_step(record=False):
+        zy.quantize_fp8(qd, blk, False, qc, qs)
+        zy.quantize_fp8(kd, blk, False, kc, ks)
+        zy.quantize_fp8(vd, blk, False, vc, vs)
+        if record:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            zy.attn_fwd_fp8(qc, kc, vc, qs, ks, vs, blk, scale, o=o8)
+            e1.record(stream)
+            ev.append((e0, e1))
+        else:
+            zy.attn_fwd_fp8(qc, kc, vc, qs, ks, vs, blk, scale, o=o8)
+
+    for _ in range(args.warmup):
+        fp8_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fp8_step(record=True)
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    attn_s = float(np.mean(attn_ms)) / 1e3
+    attn_med_s = float(np.median(attn_ms)) / 1e3
+    print(f"[bench] fp8 step {step_s * 1e3:.3f} ms, attention kernel mean {attn_s * 1e3:.3f} ms "
+          f"(median {attn_med_s * 1e3:.3f})", file=sys.stderr, flush=True)
+
+    # ---------------- BF16 attention ----------------
+    bf16 = None
+    if not args.no_bf16:
+        qb, kb, vb = qd.to(torch.bfloat16), kd.to(torch.bfloat16), vd.to(torch.bfloat16)
+        ob = torch.empty((w.B, w.Hq, w.S, w.Dv), dtype=torch.bfloat16, device=dev)
+        evb = []
+
+        def bf16_step():
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            zy.attn_fwd_bf16(qb, kb, vb, scale, o=ob)
+            e1.record(stream)
+            evb.append((e0, e1))
+
+        for _ in range(max(args.warmup // 2, 1)):
+            zy.attn_fwd_bf16(qb, kb, vb, scale, o=ob)
+        torch.cuda.synchronize()
+        bsteps = max(args.steps // 2, 1)
+        t0 = time.perf_counter()
+        for _ in range(bsteps):
+            bf16_step()
+        torch.cuda.synchronize()
+        bstep_s = (time.perf_counter() - t0) / bsteps
+        bms = [a.elapsed_time(b) for a, b in evb]
+        b_s = float(np.mean(bms)) / 1e3
+        print(f"[bench] bf16 attention kernel mean {b_s * 1e3:.3f} ms", file=sys.stderr, flush=True)
+        bf16 = {"tflops": flops / b_s / 1e12, "ms": b_s * 1e3, "ms_median": float(np.median(bms)),
+                "frac_of_bf16_peak": flops / b_s / 1e12 / PEAK_BF16, "frac_of_fp8_peak": flops / b_s / 1e12 / PEAK_FP8,
+                "peak": PEAK_BF16, "steps": bsteps, "step_ms": bstep_s * 1e3,
+                "hbm_traffic": hbm_traffic(w.name, "bf16")}
+
+    achieved = flops / attn_s / 1e12
+    line = {
+        "metric": "causal prefill attn TFLOPS + % of FP8 MFMA peak, S=32K D=128 (FP8 & BF16)",
+        "value": flops / step_s / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: causal prefill B={w.B} Hq={w.Hq} Hkv={w.Hkv} S={w.S} Dqk={w.Dqk} "
+                               f"Dv={w.Dv}, Q/K/V ~ N(0,1) float32, e4m3 scale block {blk}",
+                   "step": "quantize Q,K,V (e4m3, per-block scales) + FP8 attention",
+                   "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP8, "traffic": hbm_traffic(w.name, "fp8"),
+                     "kernel": "attn_fwd_kernel<FP8, 128>", "kernel_ms_mean": attn_s * 1e3,
+                     "kernel_ms_median": attn_med_s * 1e3},
+        "bf16": bf16,
+    }
+
+    if not args.no_cpu:
+        cpu, rows, ref_o, _ = cpu_baseline(w, q, k, v)
+        # the sampled rows also give a full-size parity figure for the timed configuration
+        got = o8[0, 0, rows].float().cpu().numpy().astype(np.float64)
+        line["cpu_baseline"] = cpu
+        line["sampled_rel_l2_fp8"] = float(np.linalg.norm(got - ref_o[0, 0]) / np.linalg.norm(ref_o[0, 0]))
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

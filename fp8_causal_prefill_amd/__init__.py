@@ -1,0 +1,130 @@
+"""Causal prefill attention for MI355X (gfx950): FP8 (e4m3, per-block scales) and BF16.
+
+A thin binding over the C ABI of libzyfa.so (include/zyfa.h). Each function checks
+that its tensors are contiguous device tensors of the right dtype and shape, then
+passes their device pointers and the current HIP stream to the library; all
+arithmetic runs in the library's HIP kernels. PyTorch provides device memory and
+streams only. There is no fallback: if libzyfa.so is missing, calls raise.
+
+Functions mirror the C entry points:
+
+* ``quantize_fp8(x, scale_block, hadamard)`` -> (codes uint8, scales float32)
+* ``attn_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, scale_block, softmax_scale)``
+  -> (o bfloat16, lse float32 or None)
+* ``attn_fwd_bf16(q, k, v, softmax_scale)`` -> (o bfloat16, lse float32 or None)
+"""
+
+import math
+
+import torch
+
+from . import _lib
+from ._lib import ZyfaError, load
+
+__all__ = ["quantize_fp8", "attn_fwd_fp8", "attn_fwd_bf16", "ZyfaError", "load", "abi_version"]
+
+
+def abi_version() -> int:
+    return load().zyfa_abi_version()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def quantize_fp8(x: torch.Tensor, scale_block: int = 128, hadamard: bool = False, codes=None, scales=None):
+    """Quantize x [B, H, S, D] (float32 or bfloat16, on the GPU) to e4m3 codes with one
+    float32 scale per (b, h, block of scale_block tokens). Returns (codes, scales)."""
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    px = _dev(x, "x", x.dtype, 4)
+    B, H, S, D = x.shape
+    nb = (S + scale_block - 1) // scale_block if scale_block > 0 else 0
+    if codes is None:
+        codes = torch.empty((B, H, S, D), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, max(nb, 1)), dtype=torch.float32, device=x.device)
+    pc = _dev(codes, "codes", torch.uint8, 4)
+    ps = _dev(scales, "scales", torch.float32, 3)
+    if tuple(codes.shape) != (B, H, S, D) or tuple(scales.shape) != (B, H, nb):
+        raise ValueError("codes / scales have the wrong shape")
+    lib = load()
+    st = lib.zyfa_quantize_fp8(px, int(x.dtype == torch.bfloat16), pc, ps, B, H, S, D, scale_block,
+                               int(bool(hadamard)), _stream())
+    _lib.check(st, "zyfa_quantize_fp8")
+    return codes, scales
+
+
+def _attn_shapes(q, k, v):
+    B, Hq, S, Dqk = q.shape
+    Bk, Hkv, Sk, Dk = k.shape
+    if (Bk, Sk, Dk) != (B, S, Dqk) or v.shape[0] != B or v.shape[1] != Hkv or v.shape[2] != S:
+        raise ValueError(f"inconsistent shapes q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    return B, Hq, Hkv, S, Dqk, v.shape[3]
+
+
+def _outputs(q, B, Hq, S, Dv, o, lse, return_lse):
+    if o is None:
+        o = torch.empty((B, Hq, S, Dv), dtype=torch.bfloat16, device=q.device)
+    po = _dev(o, "o", torch.bfloat16, 4)
+    if tuple(o.shape) != (B, Hq, S, Dv):
+        raise ValueError("o has the wrong shape")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    plse = None
+    if lse is not None:
+        plse = _dev(lse, "lse", torch.float32, 3)
+        if tuple(lse.shape) != (B, Hq, S):
+            raise ValueError("lse has the wrong shape")
+    return o, po, lse, plse
+
+
+def attn_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, scale_block: int, softmax_scale=None, o=None, lse=None,
+                 return_lse: bool = False):
+    """Causal attention on e4m3 codes (uint8 tensors [B, H, S, D]) with float32 block
+    scales [B, H, ceil(S / scale_block)]. Returns (o bfloat16 [B, Hq, S, Dv], lse or None)."""
+    pq = _dev(q, "q", torch.uint8, 4)
+    pk = _dev(k, "k", torch.uint8, 4)
+    pv = _dev(v, "v", torch.uint8, 4)
+    B, Hq, Hkv, S, Dqk, Dv = _attn_shapes(q, k, v)
+    nb = (S + scale_block - 1) // scale_block if scale_block > 0 else 0
+    psq = _dev(q_scale, "q_scale", torch.float32, 3)
+    psk = _dev(k_scale, "k_scale", torch.float32, 3)
+    psv = _dev(v_scale, "v_scale", torch.float32, 3)
+    if tuple(q_scale.shape) != (B, Hq, nb) or tuple(k_scale.shape) != (B, Hkv, nb) or tuple(v_scale.shape) != (B, Hkv, nb):
+        raise ValueError("scale tensors have the wrong shape")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(Dqk)
+    o, po, lse, plse = _outputs(q, B, Hq, S, Dv, o, lse, return_lse)
+    st = load().zyfa_attn_fwd_fp8(pq, pk, pv, psq, psk, psv, scale_block, po, plse, B, Hq, Hkv, S, Dqk, Dv,
+                                  float(softmax_scale), _stream())
+    _lib.check(st, "zyfa_attn_fwd_fp8")
+    return o, lse
+
+
+def attn_fwd_bf16(q, k, v, softmax_scale=None, o=None, lse=None, return_lse: bool = False):
+    """Causal attention on bfloat16 tensors [B, H, S, D]. Returns (o bfloat16, lse or None)."""
+    pq = _dev(q, "q", torch.bfloat16, 4)
+    pk = _dev(k, "k", torch.bfloat16, 4)
+    pv = _dev(v, "v", torch.bfloat16, 4)
+    B, Hq, Hkv, S, Dqk, Dv = _attn_shapes(q, k, v)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(Dqk)
+    o, po, lse, plse = _outputs(q, B, Hq, S, Dv, o, lse, return_lse)
+    st = load().zyfa_attn_fwd_bf16(pq, pk, pv, po, plse, B, Hq, Hkv, S, Dqk, Dv, float(softmax_scale), _stream())
+    _lib.check(st, "zyfa_attn_fwd_bf16")
+    return o, lse

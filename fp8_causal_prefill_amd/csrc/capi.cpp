@@ -1,0 +1,127 @@
+// The C ABI declared in include/zyfa.h: argument validation, dispatch, status codes.
+// Every check runs on the host before any HIP call, so an invalid request enqueues
+// no device work and touches no device state.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/zyfa.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+zyfa_status fail(zyfa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+zyfa_status ok() {
+  g_last_error[0] = '\0';
+  return ZYFA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Largest element count any tensor may have (keeps every 64-bit offset far from overflow
+// and every per-head row count within int range).
+constexpr long long kMaxElems = 1LL << 40;
+
+zyfa_status check_attn_common(const void* q, const void* k, const void* v, const void* o, const void* lse, int B,
+                              int Hq, int Hkv, int S, int Dqk, int Dv, float softmax_scale) {
+  if (!q || !k || !v || !o) return fail(ZYFA_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-null");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "B, Hq, Hkv and S must be positive (got %d, %d, %d, %d)", B, Hq, Hkv, S);
+  if (Hq % Hkv != 0) return fail(ZYFA_ERR_INVALID_ARGUMENT, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale))
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and positive");
+  if (Dqk <= 0 || Dv <= 0) return fail(ZYFA_ERR_INVALID_ARGUMENT, "head dims must be positive");
+  if ((long long)B * Hq * S * (Dqk > Dv ? Dqk : Dv) > kMaxElems)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "tensor too large");
+  if (!((Dqk == 128 && Dv == 128) || (Dqk == 192 && Dv == 128)))
+    return fail(ZYFA_ERR_UNSUPPORTED, "(Dqk, Dv) = (%d, %d) is not supported; use (128, 128) or (192, 128)", Dqk, Dv);
+  const long long n_qtiles = (S + 127) / 128;
+  if (n_qtiles * B * Hq > 0x7FFFFFFFLL) return fail(ZYFA_ERR_UNSUPPORTED, "grid too large");
+  if ((o == q || o == k || o == v) || (lse && (lse == q || lse == k || lse == v || lse == o)))
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
+  return ZYFA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int zyfa_abi_version(void) { return ZYFA_ABI_VERSION; }
+
+const char* zyfa_status_string(int status) {
+  switch (status) {
+    case ZYFA_OK: return "ZYFA_OK";
+    case ZYFA_ERR_INVALID_ARGUMENT: return "ZYFA_ERR_INVALID_ARGUMENT";
+    case ZYFA_ERR_UNSUPPORTED: return "ZYFA_ERR_UNSUPPORTED";
+    case ZYFA_ERR_LAUNCH: return "ZYFA_ERR_LAUNCH";
+    default: return "ZYFA_UNKNOWN_STATUS";
+  }
+}
+
+const char* zyfa_last_error(void) { return g_last_error; }
+
+zyfa_status zyfa_quantize_fp8(const void* x, int x_is_bf16, uint8_t* codes, float* scales, int B, int H, int S,
+                              int D, int scale_block, int hadamard, void* stream) {
+  if (!x || !codes || !scales) return fail(ZYFA_ERR_INVALID_ARGUMENT, "x, codes and scales must be non-null");
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales))
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  if (x_is_bf16 != 0 && x_is_bf16 != 1) return fail(ZYFA_ERR_INVALID_ARGUMENT, "x_is_bf16 must be 0 or 1");
+  if (hadamard != 0 && hadamard != 1) return fail(ZYFA_ERR_INVALID_ARGUMENT, "hadamard must be 0 or 1");
+  if (B <= 0 || H <= 0 || S <= 0 || D <= 0)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "B, H, S and D must be positive (got %d, %d, %d, %d)", B, H, S, D);
+  if (scale_block != 64 && scale_block != 128)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "scale_block must be 64 or 128 (got %d)", scale_block);
+  if ((long long)B * H * S * D > kMaxElems) return fail(ZYFA_ERR_INVALID_ARGUMENT, "tensor too large");
+  if (D != 128 && D != 192) return fail(ZYFA_ERR_UNSUPPORTED, "D = %d is not supported; use 128 or 192", D);
+  if (hadamard && D != 128) return fail(ZYFA_ERR_UNSUPPORTED, "the Hadamard rotation requires D = 128");
+  const long long nb = (S + scale_block - 1) / scale_block;
+  if (nb * B * H > 0x7FFFFFFFLL) return fail(ZYFA_ERR_UNSUPPORTED, "grid too large");
+  if ((const void*)codes == x || (const void*)scales == x || (const void*)scales == (const void*)codes)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
+
+  zyfa::QuantArgs a{x, x_is_bf16, codes, scales, B, H, S, D, scale_block, hadamard};
+  hipError_t e = zyfa::launch_quantize_fp8(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ZYFA_ERR_LAUNCH, "quantize launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+zyfa_status zyfa_attn_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_scale,
+                              const float* k_scale, const float* v_scale, int scale_block, uint16_t* o, float* lse,
+                              int B, int Hq, int Hkv, int S, int Dqk, int Dv, float softmax_scale, void* stream) {
+  zyfa_status st = check_attn_common(q, k, v, o, lse, B, Hq, Hkv, S, Dqk, Dv, softmax_scale);
+  if (st != ZYFA_OK) return st;
+  if (!q_scale || !k_scale || !v_scale) return fail(ZYFA_ERR_INVALID_ARGUMENT, "scale pointers must be non-null");
+  if (!aligned16(q_scale) || !aligned16(k_scale) || !aligned16(v_scale))
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  if (scale_block != 64 && scale_block != 128)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "scale_block must be 64 or 128 (got %d)", scale_block);
+
+  zyfa::AttnArgs a{q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, S, Dqk, Dv, scale_block, softmax_scale};
+  hipError_t e = zyfa::launch_attn_fwd_fp8(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ZYFA_ERR_LAUNCH, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+zyfa_status zyfa_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                               int B, int Hq, int Hkv, int S, int Dqk, int Dv, float softmax_scale, void* stream) {
+  zyfa_status st = check_attn_common(q, k, v, o, lse, B, Hq, Hkv, S, Dqk, Dv, softmax_scale);
+  if (st != ZYFA_OK) return st;
+  zyfa::AttnArgs a{q, k, v, nullptr, nullptr, nullptr, o, lse, B, Hq, Hkv, S, Dqk, Dv, 0, softmax_scale};
+  hipError_t e = zyfa::launch_attn_fwd_bf16(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ZYFA_ERR_LAUNCH, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

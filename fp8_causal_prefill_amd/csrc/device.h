@@ -1,0 +1,96 @@
+// Device-side types and gfx950 instruction wrappers shared by the kernels.
+//
+// Operand layouts of the CDNA4 matrix instructions used here (wave of 64 lanes,
+// lane l, h = l / 32):
+//
+//  * v_mfma_*_32x32x64_f8f6f4 (e4m3): each lane holds 32 bytes of A (row l % 32)
+//    and 32 bytes of B (column l % 32) along K. An unscaled product only needs
+//    A and B to agree on which K position each byte is. With scales, the two
+//    32-wide scale blocks of K are {bytes 0-15 of lanes i and i+32} (scale from
+//    lane i) and {bytes 16-31 of lanes i and i+32} (scale from lane i+32), for
+//    A row / B column i; the scale is an E8M0 exponent in byte 0 of a VGPR.
+//  * v_mfma_f32_32x32x16_bf16: 8 bf16 of A (row l % 32) and of B (column l % 32).
+//  * 32x32 f32 accumulator: register r of lane l holds row 8(r/4) + 4h + r%4,
+//    column l % 32.
+//  * ds_read_b64_tr_b8: in each group of 16 lanes, lane 2r+c addresses 8 bytes
+//    (half c of row r of an 8-row x 16-byte block); lane i receives byte i of
+//    rows 0..7. ds_read_b64_tr_b16: lane 4r+c addresses 4 bf16 (quarter c of row
+//    r of a 4-row x 16-element block); lane i receives element i of rows 0..3.
+//  * v_permlane32_swap: exchanges a VGPR between lane i and lane i+32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace zyfa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) v4bf lds_v4bf;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kE8M0One = 127;  // E8M0 exponent code of 1.0
+
+// D += A * B on e4m3 with per-lane E8M0 scales (see the layout note above).
+__device__ __forceinline__ v16f mfma_fp8_scaled(const v8i& a, const v8i& b, const v16f& c, int scale_a,
+                                                int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
+}
+
+// D += A * B on e4m3, no scaling.
+__device__ __forceinline__ v16f mfma_fp8(const v8i& a, const v8i& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ v16f mfma_bf16(const v8bf& a, const v8bf& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Keep a value in a VGPR so the compiler cannot fold it into an instruction constant
+// (scale operands of the scaled MFMA must come from registers).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// max of a value across lanes i and i+32.
+__device__ __forceinline__ float max_across_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                            false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+
+// sum of a value across lanes i and i+32.
+__device__ __forceinline__ float sum_across_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                            false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Two floats -> two e4m3 codes (round-to-nearest-even; values must lie within +-448:
+// the hardware conversion does not saturate), written to the low (HIGH = false) or
+// high (HIGH = true) 16 bits of `old`.
+template <bool HIGH>
+__device__ __forceinline__ int cvt_pk_fp8(float a, float b, int old) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HIGH);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  // (__bf16) conversion is round-to-nearest-even on gfx950 (v_cvt_pk_bf16_f32).
+  __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace zyfa

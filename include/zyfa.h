@@ -1,0 +1,151 @@
+/*
+ * zyfa.h - C ABI of the MI355X (gfx950) causal prefill attention library.
+ *
+ * The library computes causal forward ("prefill") attention
+ *
+ *     O = softmax(Q K^T * softmax_scale + causal mask) V
+ *
+ * for equal query and key lengths, in two precisions:
+ *
+ *   - FP8: Q, K, V as OCP e4m3 (E4M3FN) codes with one float32 scale per
+ *     (batch, head, block of scale_block tokens);
+ *   - BF16: Q, K, V as bfloat16.
+ *
+ * Head shapes: Dqk = Dv = 128 (query heads may share key/value heads: GQA), and
+ * the MLA shape Dqk = 192, Dv = 128.
+ *
+ * Source: "ZYFA: Fast and Accurate FP8 Attention on AMD MI355X" -- Introduction
+ * (the operation and the two head shapes, footnote 4 for MLA), "Methodology and
+ * Limitations" (causal, equal query and key lengths, no decode / paged KV /
+ * variable-length batches), "Per-Block Scaling and Normalization by the Rounded
+ * Row Sum" (the FP8 probability scaling and normalisation), footnote 2 (inputs
+ * are quantized in separate passes, with an optional Hadamard rotation of Q
+ * and K fused into the quantization).
+ *
+ * Conventions shared by every entry point:
+ *
+ *   Layout     Every tensor is dense row-major [B, H, S, D] (D fastest), the
+ *              order of PyTorch's scaled_dot_product_attention. Scales are dense
+ *              [B, H, nb] with nb = ceil(S / scale_block). Query head h reads
+ *              key/value head h / (Hq / Hkv).
+ *   Memory     All pointers are device pointers owned by the caller and must be
+ *              16-byte aligned. Outputs must not alias inputs. The library never
+ *              allocates, frees or synchronises.
+ *   Streams    `stream` is a hipStream_t passed as void* (NULL = the null stream);
+ *              all work is enqueued on it and the call returns without waiting.
+ *   Errors     Argument checks happen on the host before any device work; a
+ *              failing call enqueues nothing. ZYFA_ERR_LAUNCH reports a failed
+ *              kernel launch. Faults inside a kernel surface at the caller's next
+ *              synchronisation. Inputs are not scanned for NaN / Inf; e4m3 NaN
+ *              codes (0x7F, 0xFF) give undefined output.
+ *   Threads    The library keeps no state between calls; calls are thread-safe.
+ *              zyfa_last_error() reads a thread-local message.
+ */
+#ifndef ZYFA_H
+#define ZYFA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZYFA_ABI_VERSION 1
+
+typedef enum zyfa_status {
+  ZYFA_OK = 0,
+  ZYFA_ERR_INVALID_ARGUMENT = 1, /* null / misaligned pointer, bad size, bad scale */
+  ZYFA_ERR_UNSUPPORTED = 2,      /* a valid request this build has no kernel for */
+  ZYFA_ERR_LAUNCH = 3            /* the HIP runtime rejected the kernel launch */
+} zyfa_status;
+
+/* ABI version of the loaded library (ZYFA_ABI_VERSION of its build). */
+int zyfa_abi_version(void);
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char* zyfa_status_string(int status);
+
+/* Message describing why the calling thread's most recent failing call failed
+ * (empty string if none). Valid until the thread's next library call. */
+const char* zyfa_last_error(void);
+
+/*
+ * zyfa_quantize_fp8 -- quantize a tensor to e4m3 codes with per-block scales.
+ *
+ * Source: footnote 2 and section "FP8 Error in Full-Model Inference" of the ZYFA
+ * page (a separate quantization pass; an optional Hadamard rotation of Q and K
+ * over the head dimension, fused into that pass); FP8 GEMM on CDNA4 blog,
+ * sections 2.2-2.3 (absmax scaling with a zero guard, round-to-nearest-even).
+ *
+ *   x            [B, H, S, D] float32 (x_is_bf16 = 0) or bfloat16 (x_is_bf16 = 1).
+ *   codes        out: [B, H, S, D] e4m3 codes.
+ *   scales       out: [B, H, nb] float32, nb = ceil(S / scale_block).
+ *   scale_block  tokens per scale: 64 or 128.
+ *   hadamard     0: none. 1: first rotate every row of D values by the orthonormal
+ *                Sylvester Hadamard matrix H_D / sqrt(D) (requires D == 128).
+ *
+ * For each (b, h, token block): amax = max |y| over the block's tokens and all D
+ * channels (y = x, or the rotated row); s = the least power of two with
+ * amax / s <= 448 (s >= 2^-126; s = 1 if amax == 0), the E8M0 form that the
+ * scaled FP8 matrix instruction applies exactly; code = round-to-nearest-even
+ * e4m3 of the exact quotient y / s, saturated to +-448. Without rotation the
+ * result is bit-exact to that definition; with rotation y is computed in float32
+ * by a fast Walsh-Hadamard transform.
+ * The dequantized value of an element is decode(code) * s.
+ */
+zyfa_status zyfa_quantize_fp8(const void* x, int x_is_bf16, uint8_t* codes, float* scales, int B, int H,
+                              int S, int D, int scale_block, int hadamard, void* stream);
+
+/*
+ * zyfa_attn_fwd_fp8 -- causal attention on e4m3 inputs.
+ *
+ * Source: ZYFA page, sections "Precision and Underflow of FP8 Probabilities" and
+ * "Per-Block Scaling and Normalization by the Rounded Row Sum".
+ *
+ *   q, k, v      e4m3 codes: q [B, Hq, S, Dqk], k [B, Hkv, S, Dqk], v [B, Hkv, S, Dv].
+ *   q_scale      [B, Hq, nb] float32; k_scale, v_scale [B, Hkv, nb] float32; each
+ *                finite and > 0. Dequantized input = decode(code) * scale. Any
+ *                positive scale is accepted; power-of-two V scales (as written by
+ *                zyfa_quantize_fp8) are applied exactly by the matrix instruction,
+ *                while the mantissa of other V scales is folded into the
+ *                probabilities before their rounding to e4m3.
+ *   scale_block  tokens per scale: 64 or 128.
+ *   o            out: [B, Hq, S, Dv] bfloat16 (round-to-nearest-even).
+ *   lse          out, may be NULL: [B, Hq, S] float32, natural-log log-sum-exp of
+ *                the scaled scores of each query row.
+ *   softmax_scale  multiplies Q K^T; finite and > 0 (usually 1/sqrt(Dqk)).
+ *
+ * Supported: (Dqk, Dv) in {(128, 128), (192, 128)}, Hq % Hkv == 0, any S >= 1.
+ * Method: scores on the FP8 matrix cores; probabilities are formed with a
+ * base-2 exponential, and every (query row, 64-key block) of probabilities is
+ * multiplied by a power of two that puts its largest value in [1, 2) before the
+ * round-to-nearest-even conversion to e4m3; the power of two is divided back out
+ * by the scaled FP8 matrix instruction. Each row is normalised by the sum of the
+ * rounded probabilities that multiply V, so the output is a weighted average
+ * whose weights sum to one.
+ */
+zyfa_status zyfa_attn_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_scale,
+                              const float* k_scale, const float* v_scale, int scale_block, uint16_t* o,
+                              float* lse, int B, int Hq, int Hkv, int S, int Dqk, int Dv, float softmax_scale,
+                              void* stream);
+
+/*
+ * zyfa_attn_fwd_bf16 -- causal attention on bfloat16 inputs.
+ *
+ * Source: ZYFA page, Introduction and section "Throughput on Gaussian Inputs"
+ * (the BF16 kernels next to the FP8 ones).
+ *
+ *   q [B, Hq, S, Dqk], k [B, Hkv, S, Dqk], v [B, Hkv, S, Dv]: bfloat16 bit patterns.
+ *   o out [B, Hq, S, Dv] bfloat16; lse out (may be NULL) [B, Hq, S] float32.
+ *
+ * Same shapes, scale and error rules as zyfa_attn_fwd_fp8. Probabilities are
+ * rounded to bfloat16 for the P V product; the row sum is accumulated in float32.
+ */
+zyfa_status zyfa_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                               int B, int Hq, int Hkv, int S, int Dqk, int Dv, float softmax_scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZYFA_H */

@@ -10,12 +10,19 @@ The pages do not give the scale granularity or formula. The readings used here:
 
 * one float32 scale per (batch, head, block of ``block`` consecutive tokens),
   shared by all head-dim channels; the last block may be shorter;
-* amax = max |x| over the block; s = fl32(amax / 448), or s = 1 when
-  amax == 0 (the zero guard of the FP8 GEMM on CDNA4 blog, section 2.2);
-* code = e4m3(fl32(x / s)): a correctly rounded float32 division, then
+* amax = max |x| over the block; s = the smallest power of two with
+  amax / s <= 448 (at least 2^-126, a normal float32), or s = 1 when amax == 0 (absmax scaling with the zero guard
+  of the FP8 GEMM on CDNA4 blog, section 2.2, with the scale restricted to a
+  power of two, the E8M0 form that the ZYFA page's scaled FP8 matrix
+  instruction applies exactly: section "Per-Block Scaling and Normalization by
+  the Rounded Row Sum");
+* code = e4m3(x / s): the quotient is exact (s is a power of two), then
   round-to-nearest-even to e4m3 with saturation (blog section 2.3).
 
-The dequantized value of an element is decode(code) * s, exact in float64.
+The e4m3 grid is the same in every binade, so a power-of-two scale gives the
+same relative precision to all normal values as amax / 448 would; the largest
+element lands in (224, 448]. The dequantized value of an element is
+decode(code) * s, exact in float64.
 """
 
 import numpy as np
@@ -33,10 +40,16 @@ def quantize_blocks(x, block):
     scales = np.empty((B, H, nb), dtype=np.float32)
     for j in range(nb):
         blk = x[:, :, j * block:(j + 1) * block, :]
-        amax = np.abs(blk).max(axis=(2, 3))  # exact: a max of float32 magnitudes
-        s = amax / np.float32(E4M3_MAX)  # float32 / float32 -> correctly rounded float32
-        s = np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
-        y = blk / s[:, :, None, None]  # correctly rounded float32 division
+        amax = np.abs(blk).max(axis=(2, 3)).astype(np.float64)  # exact: a max of float32 magnitudes
+        s = np.ones(amax.shape)
+        nz = amax > 0
+        k = np.ceil(np.log2(amax[nz] / E4M3_MAX))
+        # make k exactly the least integer with amax <= 448 * 2^k (guards log2 rounding)
+        k = np.where(amax[nz] > E4M3_MAX * np.exp2(k), k + 1, k)
+        k = np.where(amax[nz] <= E4M3_MAX * np.exp2(k - 1), k - 1, k)
+        s[nz] = np.exp2(np.maximum(k, -126))  # keep the scale a normal float32
+        s = s.astype(np.float32)
+        y = blk.astype(np.float64) / s[:, :, None, None]  # exact: division by a power of two
         codes[:, :, j * block:(j + 1) * block, :] = e4m3_encode(y)
         scales[:, :, j] = s
     return codes, scales

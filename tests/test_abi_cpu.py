@@ -1,0 +1,107 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point that
+include/zyfa.h declares, and rejects invalid requests on the host before any HIP
+call (fake, never-dereferenced pointers are used; no request here is valid, so no
+kernel is ever launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp8_causal_prefill_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "zyfa.h")
+
+P = 0x10000   # a 16-byte-aligned fake device address (never dereferenced)
+P2 = 0x20000
+P3 = 0x30000
+P4 = 0x40000
+P5 = 0x50000
+P6 = 0x60000
+P7 = 0x70000
+MIS = 0x10008  # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(zyfa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == {"zyfa_abi_version", "zyfa_status_string", "zyfa_last_error", "zyfa_quantize_fp8",
+                          "zyfa_attn_fwd_fp8", "zyfa_attn_fwd_bf16"}
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.zyfa_abi_version() == 1
+    assert lib.zyfa_status_string(0) == b"ZYFA_OK"
+    assert lib.zyfa_status_string(1) == b"ZYFA_ERR_INVALID_ARGUMENT"
+    assert lib.zyfa_status_string(2) == b"ZYFA_ERR_UNSUPPORTED"
+    assert lib.zyfa_status_string(3) == b"ZYFA_ERR_LAUNCH"
+    assert lib.zyfa_status_string(99) == b"ZYFA_UNKNOWN_STATUS"
+
+
+def fp8(lib, q=P, k=P2, v=P3, qs=P4, ks=P5, vs=P6, blk=128, o=P7, lse=None, B=1, Hq=4, Hkv=2, S=256, Dqk=128,
+        Dv=128, scale=0.088):
+    return lib.zyfa_attn_fwd_fp8(q, k, v, qs, ks, vs, blk, o, lse, B, Hq, Hkv, S, Dqk, Dv, scale, None)
+
+
+def bf16(lib, q=P, k=P2, v=P3, o=P7, lse=None, B=1, Hq=4, Hkv=2, S=256, Dqk=128, Dv=128, scale=0.088):
+    return lib.zyfa_attn_fwd_bf16(q, k, v, o, lse, B, Hq, Hkv, S, Dqk, Dv, scale, None)
+
+
+INVALID = _lib.ERR_INVALID_ARGUMENT
+UNSUPPORTED = _lib.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(o=None), INVALID),
+    (dict(q=MIS), INVALID), (dict(o=MIS), INVALID), (dict(lse=MIS), INVALID),
+    (dict(B=0), INVALID), (dict(Hq=0), INVALID), (dict(Hkv=0), INVALID), (dict(S=0), INVALID), (dict(S=-5), INVALID),
+    (dict(Hq=6, Hkv=4), INVALID),
+    (dict(scale=0.0), INVALID), (dict(scale=-1.0), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(Dqk=64, Dv=64), UNSUPPORTED), (dict(Dqk=192, Dv=192), UNSUPPORTED), (dict(Dqk=128, Dv=192), UNSUPPORTED),
+    (dict(o=P), INVALID),  # output aliases q
+])
+def test_attention_argument_checks(lib, kw, expect):
+    assert bf16(lib, **kw) == expect
+    assert lib.zyfa_last_error() != b""
+    assert fp8(lib, **kw) == expect
+
+
+@pytest.mark.parametrize("kw", [dict(qs=None), dict(ks=None), dict(vs=None), dict(vs=MIS), dict(blk=32),
+                                dict(blk=0), dict(blk=256)])
+def test_fp8_scale_checks(lib, kw):
+    assert fp8(lib, **kw) == INVALID
+
+
+def quant(lib, x=P, bf=0, codes=P2, scales=P3, B=1, H=2, S=100, D=128, blk=64, had=0):
+    return lib.zyfa_quantize_fp8(x, bf, codes, scales, B, H, S, D, blk, had, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(x=None), INVALID), (dict(codes=None), INVALID), (dict(scales=None), INVALID), (dict(x=MIS), INVALID),
+    (dict(bf=2), INVALID), (dict(had=3), INVALID), (dict(B=0), INVALID), (dict(S=0), INVALID), (dict(D=0), INVALID),
+    (dict(blk=100), INVALID), (dict(D=64), UNSUPPORTED), (dict(D=192, had=1), UNSUPPORTED), (dict(codes=P), INVALID),
+])
+def test_quantize_argument_checks(lib, kw, expect):
+    assert quant(lib, **kw) == expect
+
+
+def test_binding_raises_without_device_tensors():
+    import torch
+    import fp8_causal_prefill_amd as z
+    with pytest.raises(ValueError):
+        z.attn_fwd_bf16(torch.zeros(1, 1, 128, 128, dtype=torch.bfloat16), torch.zeros(1, 1, 128, 128, dtype=torch.bfloat16),
+                        torch.zeros(1, 1, 128, 128, dtype=torch.bfloat16))

@@ -1,0 +1,178 @@
+"""GPU attention kernels against the fp64 oracle, element by element, on the same
+seeded inputs, plus the exact special cases the method has.
+
+Bars (relative L2 over the whole output tensor, O in bfloat16 upcast to float64):
+BF16 <= 5e-3, FP8 <= 3e-2. FP8 inputs are quantized on the GPU and the codes are
+first checked bit-exact against the oracle's quantizer, so both sides attend over
+the same dequantized values."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_causal_prefill_amd as zy
+from oracle import causal_attention, dequantize_blocks, e4m3_decode, quantize_blocks
+from workloads import custom, generate
+from tests.paths import (gpu_bf16, gpu_fp8, oracle_attention_from_codes, oracle_bf16, oracle_inputs_fp8, rel_l2,
+                         to_dev, bf16_from_f64)
+
+pytestmark = pytest.mark.gpu
+
+BF16_BAR = 5e-3
+FP8_BAR = 3e-2
+
+SHAPES = [
+    # (B, Hq, Hkv, S, Dqk, Dv, block)
+    (1, 1, 1, 128, 128, 128, 64),     # the tiny workload's shape
+    (1, 4, 4, 1024, 128, 128, 128),   # several query tiles, MHA
+    (2, 8, 2, 333, 128, 128, 64),     # GQA, ragged S, B = 2
+    (1, 4, 1, 64, 128, 128, 128),     # S below one query tile
+    (1, 2, 2, 1, 128, 128, 64),       # a single token
+    (1, 4, 4, 300, 192, 128, 128),    # MLA head shape, ragged
+    (1, 2, 2, 513, 192, 128, 64),     # MLA, one row past a tile boundary
+]
+
+
+def _case(shape, **kw):
+    print("case:", shape, kw, flush=True)
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_bf16_parity(shape):
+    B, Hq, Hkv, S, Dqk, Dv, _ = shape
+    _case(shape)
+    q, k, v = generate(custom(B, Hq, Hkv, S, Dqk, Dv, wid=500), seed=S)
+    scale = 1 / math.sqrt(Dqk)
+    o, lse = gpu_bf16(q, k, v, scale)
+    ro, rlse, _ = oracle_bf16(q, k, v, scale)
+    err = rel_l2(o, ro)
+    print(f"bf16 rel-L2 {err:.3e}")
+    assert err <= BF16_BAR
+    assert np.max(np.abs(lse - rlse)) < 1e-3
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_fp8_parity(shape):
+    B, Hq, Hkv, S, Dqk, Dv, block = shape
+    _case(shape)
+    q, k, v = generate(custom(B, Hq, Hkv, S, Dqk, Dv, wid=600), seed=S)
+    scale = 1 / math.sqrt(Dqk)
+    o, lse, parts = gpu_fp8(q, k, v, block, scale=scale)
+    ref_parts = oracle_inputs_fp8(q, k, v, block)
+    for got, ref in zip(parts, ref_parts):
+        assert np.array_equal(got, ref)  # the kernel reads exactly the oracle's codes and scales
+    ro, rlse = oracle_attention_from_codes(ref_parts, block, scale)
+    err = rel_l2(o, ro)
+    print(f"fp8 rel-L2 {err:.3e}")
+    assert err <= FP8_BAR
+    # worst case: every weight of a row rounded by the largest e4m3 relative error, ln(1 + 2^-4)
+    assert np.max(np.abs(lse - rlse)) < 0.062
+
+
+def test_fp8_activation_like_with_and_without_rotation():
+    w = custom(1, 8, 2, 700, 128, 128, dist="activation", scale_block=128, wid=700)
+    q, k, v = generate(w, seed=0)
+    for hadamard in (False, True):
+        _case("act", hadamard=hadamard)
+        o, _, parts = gpu_fp8(q, k, v, 128, hadamard=hadamard)
+        ro, _ = oracle_attention_from_codes(parts, 128, w.softmax_scale)
+        err = rel_l2(o, ro)
+        print(f"fp8 act hadamard={hadamard} rel-L2 {err:.3e}")
+        assert err <= FP8_BAR
+
+
+def _fp8_call(qc, kc, vc, qs, ks, vs, block, scale=None):
+    o, lse = zy.attn_fwd_fp8(qc, kc, vc, qs, ks, vs, block, scale, return_lse=True)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _quantized(B, Hq, Hkv, S, D, block, seed):
+    q, k, v = generate(custom(B, Hq, Hkv, S, D, D, wid=800), seed=seed)
+    qc, qs = quantize_blocks(q, block)
+    kc, ks = quantize_blocks(k, block)
+    vc, vs = quantize_blocks(v, block)
+    return [to_dev(x) for x in (qc, kc, vc, qs, ks, vs)]
+
+
+def test_fp8_constant_v_gives_exactly_one():
+    # V == 1.0 (code 0x38, scale 1): the rounded-row-sum normalisation makes every
+    # output exactly 1; a kernel dividing by the unrounded sum would fall short of 1.
+    qc, kc, vc, qs, ks, vs = _quantized(1, 4, 2, 600, 128, 64, seed=1)
+    vc = torch.full_like(vc, 0x38)
+    vs = torch.ones_like(vs)
+    o, _ = _fp8_call(qc, kc, vc, qs, ks, vs, 64)
+    assert torch.all(o.float() == 1.0)
+
+
+def test_fp8_zero_q_gives_prefix_mean_with_pow2_v_scales():
+    # Q = 0: all scores equal, every probability is exactly 1 after the block scaling
+    # (V scales are powers of two here), so O is the prefix mean of V up to float32
+    # accumulation and the bfloat16 output rounding.
+    qc, kc, vc, qs, ks, vs = _quantized(1, 2, 2, 500, 128, 128, seed=2)
+    qc = torch.zeros_like(qc)
+    vs = torch.exp2(torch.round(torch.log2(vs)))
+    o, _ = _fp8_call(qc, kc, vc, qs, ks, vs, 128)
+    vd = dequantize_blocks(vc.cpu().numpy(), vs.cpu().numpy(), 128)
+    ref = np.cumsum(vd, axis=2) / np.arange(1, 501)[None, None, :, None]
+    err = rel_l2(bf16_from_f64(o), ref)
+    print("prefix-mean rel-L2", err)
+    assert err < 4e-3
+
+
+def test_fp8_row0_returns_v0_and_v_scale_doubling_is_exact():
+    qc, kc, vc, qs, ks, vs = _quantized(1, 4, 4, 256, 128, 64, seed=3)
+    o1, _ = _fp8_call(qc, kc, vc, qs, ks, vs, 64)
+    v0 = e4m3_decode(vc[:, :, 0].cpu().numpy()) * vs[:, :, 0:1].cpu().numpy()
+    got = bf16_from_f64(o1[:, :, 0])
+    ulp = np.maximum(np.abs(v0), 2.0 ** -126) * 2.0 ** -7
+    assert np.all(np.abs(got - v0) <= ulp)
+    o2, _ = _fp8_call(qc, kc, vc, qs, ks, vs * 2, 64)
+    assert torch.equal(o2.float(), 2 * o1.float())
+
+
+def test_fp8_causal_leak_probe():
+    # Changing keys and values after position `cut` must not change rows <= cut (bitwise).
+    cut = 150
+    qc, kc, vc, qs, ks, vs = _quantized(1, 2, 2, 320, 128, 64, seed=4)
+    o1, l1 = _fp8_call(qc, kc, vc, qs, ks, vs, 64)
+    kc2, vc2 = kc.clone(), vc.clone()
+    kc2[:, :, cut + 1:] = 0x7E   # +448: scores far above anything in the past
+    vc2[:, :, cut + 1:] = 0xFE   # -448
+    o2, l2 = _fp8_call(qc, kc2, vc2, qs, ks, vs, 64)
+    assert torch.equal(o1[:, :, :cut + 1], o2[:, :, :cut + 1])
+    assert torch.equal(l1[:, :, :cut + 1], l2[:, :, :cut + 1])
+    assert not torch.equal(o1[:, :, cut + 1:], o2[:, :, cut + 1:])
+
+
+def test_gqa_equals_mha_with_repeated_kv_bitwise():
+    qc, kc, vc, qs, ks, vs = _quantized(1, 8, 2, 200, 128, 64, seed=5)
+    o_gqa, _ = _fp8_call(qc, kc, vc, qs, ks, vs, 64)
+    rep = lambda t: t.repeat_interleave(4, dim=1).contiguous()
+    o_mha, _ = _fp8_call(qc, rep(kc), rep(vc), qs, rep(ks), rep(vs), 64)
+    assert torch.equal(o_gqa, o_mha)
+    q, k, v = generate(custom(1, 8, 2, 200, 128, 128, wid=801), seed=0)
+    tb = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()
+    a, _ = zy.attn_fwd_bf16(tb(q), tb(k), tb(v))
+    b, _ = zy.attn_fwd_bf16(tb(q), tb(np.repeat(k, 4, axis=1)), tb(np.repeat(v, 4, axis=1)))
+    assert torch.equal(a, b)
+
+
+def test_deterministic_and_stream_ordered():
+    qc, kc, vc, qs, ks, vs = _quantized(2, 4, 2, 700, 128, 128, seed=6)
+    o1, l1 = _fp8_call(qc, kc, vc, qs, ks, vs, 128)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2, l2 = zy.attn_fwd_fp8(qc, kc, vc, qs, ks, vs, 128, return_lse=True)
+    s.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_bf16_constant_v():
+    q, k, _ = generate(custom(1, 2, 2, 400, 128, 128, wid=802), seed=7)
+    tb = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()
+    v = torch.ones((1, 2, 400, 128), dtype=torch.bfloat16, device="cuda")
+    o, _ = zy.attn_fwd_bf16(tb(q), tb(k), v)
+    assert torch.max(torch.abs(o.float() - 1.0)).item() <= 2.0 ** -8

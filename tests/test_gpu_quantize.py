@@ -1,0 +1,81 @@
+"""GPU quantizer (zyfa_quantize_fp8) against the oracle's block quantizer.
+
+Without rotation the codes and scales are an integer / exactly-rounded result and
+must match bit for bit. With the Hadamard rotation the GPU rotates in float32 by a
+fast Walsh-Hadamard transform while the oracle rotates in float64, so a code may
+differ where the rotated value sits on a rounding boundary, and a power-of-two
+scale where the block absmax sits on a binade boundary: every GPU code must still
+be a correct rounding of the oracle's exactly rotated value (over the GPU's scale)
+up to float32 noise."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import quantize_blocks, hadamard_rotate, e4m3_decode
+from workloads import custom, generate
+from tests.paths import gpu_quantize, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _print_case(**kw):
+    print("case:", ", ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+@pytest.mark.parametrize("S", [128, 1, 63, 64, 65, 300, 1000])
+@pytest.mark.parametrize("block", [64, 128])
+@pytest.mark.parametrize("D", [128, 192])
+def test_quantize_bit_exact_fp32(S, block, D):
+    _print_case(S=S, block=block, D=D)
+    x, _, _ = generate(custom(2, 3, 3, S, D, D, wid=200 + S), seed=1)
+    x = x * np.float32(2.5)
+    codes, scales = gpu_quantize(x, block)
+    rc, rs = quantize_blocks(x, block)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_quantize_bit_exact_bf16_input():
+    x, _, _ = generate(custom(1, 4, 4, 257, 128, 128, wid=301), seed=2)
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    codes, scales = __import__("fp8_causal_prefill_amd").quantize_fp8(xb.to("cuda"), 128)
+    rc, rs = quantize_blocks(xb.float().numpy(), 128)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_quantize_zero_block_and_extremes():
+    x = np.zeros((1, 1, 256, 128), np.float32)
+    x[0, 0, 128:] = np.random.default_rng(3).standard_normal((128, 128)).astype(np.float32) * 1e-30
+    x[0, 0, 200, 5] = 3e38
+    codes, scales = gpu_quantize(x, 64)
+    rc, rs = quantize_blocks(x, 64)
+    assert scales[0, 0, 0].item() == 1.0
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+@pytest.mark.parametrize("S,block", [(128, 64), (333, 128)])
+def test_quantize_hadamard(S, block):
+    _print_case(S=S, block=block)
+    w = custom(1, 2, 2, S, 128, 128, dist="activation", wid=400 + S)
+    x, _, _ = generate(w, seed=4)
+    codes, scales = gpu_quantize(x, block, hadamard=True)
+    codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
+    y = hadamard_rotate(x)  # exact rotation (float64)
+    rc, rs = quantize_blocks(y.astype(np.float32), block)
+    # scales: powers of two from the block absmax of a float32-computed rotation; they can
+    # differ from the exact rotation's only where that absmax sits on a binade boundary
+    ratio = scales.astype(np.float64) / rs
+    assert np.all((ratio == 1.0) | (ratio == 2.0) | (ratio == 0.5))
+    assert np.mean(ratio != 1.0) < 0.05
+    # every GPU code decodes to a nearest e4m3 value of y / s up to float32 noise in y
+    s = np.repeat(scales.astype(np.float64), block, axis=2)[:, :, :S, None]
+    t = y / s
+    dec = e4m3_decode(codes)
+    err = np.abs(dec - t)
+    half_ulp = np.maximum(np.abs(t) * 2.0 ** -4, 2.0 ** -10)
+    assert np.all(err <= half_ulp * (1 + 1e-5) + np.abs(t) * 1e-6)
+    mismatch = np.mean(codes != rc)
+    assert mismatch < 1e-3, mismatch

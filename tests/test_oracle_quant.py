@@ -20,20 +20,35 @@ def _x(shape, seed=0):
 
 @pytest.mark.parametrize("block", [64, 128])
 @pytest.mark.parametrize("S", [128, 200, 64, 1])
-def test_scale_is_absmax_over_448(block, S):
-    x = _x((2, 3, S, 128))
+def test_scale_is_least_power_of_two_over_absmax(block, S):
+    x = _x((2, 3, S, 128)) * np.float32(3.7)
     codes, scales = quantize_blocks(x, block)
     nb = (S + block - 1) // block
     assert scales.shape == (2, 3, nb) and scales.dtype == np.float32
+    m, e = np.frexp(scales.astype(np.float64))
+    assert np.all(m == 0.5)  # powers of two
     for j in range(nb):
+        amax = np.abs(x[:, :, j * block:(j + 1) * block]).max(axis=(2, 3)).astype(np.float64)
+        s = scales[:, :, j].astype(np.float64)
+        assert np.all(amax / s <= 448.0) and np.all(amax / s > 224.0)  # the least such power of two
+        # the largest-magnitude element of each block is coded with the exact quotient's rounding
         blk = x[:, :, j * block:(j + 1) * block]
-        amax = np.abs(blk).max(axis=(2, 3))
-        assert np.array_equal(scales[:, :, j], (amax / np.float32(448.0)).astype(np.float32))
-        # the largest-magnitude element of each block is coded as +-448 (0x7E / 0xFE)
         for b in range(2):
             for h in range(3):
                 i = np.unravel_index(np.argmax(np.abs(blk[b, h])), blk[b, h].shape)
-                assert codes[b, h, j * block + i[0], i[1]] & 0x7F == 0x7E
+                c = codes[b, h, j * block + i[0], i[1]]
+                assert abs(e4m3_decode(c)) >= 224.0
+
+
+def test_tiny_and_huge_blocks():
+    x = np.zeros((1, 1, 192, 128), np.float32)
+    x[0, 0, :64, 0] = 1e-42           # denormal float32: the scale stays at 2^-126
+    x[0, 0, 64:128, 3] = 3.0e38
+    x[0, 0, 128:, 5] = 448.0           # exactly 448 * 2^0
+    codes, scales = quantize_blocks(x, 64)
+    assert scales[0, 0, 0] == np.float32(2.0 ** -126)
+    assert scales[0, 0, 1] == np.float32(2.0 ** 120) and 3.0e38 / 2.0 ** 120 <= 448
+    assert scales[0, 0, 2] == 1.0 and codes[0, 0, 128, 5] == 0x7E
 
 
 def test_zero_block_guard():
