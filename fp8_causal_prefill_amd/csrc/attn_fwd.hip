@@ -3,36 +3,51 @@
 // "ZYFA: Fast and Accurate FP8 Attention on AMD MI355X":
 //  * Introduction: FlashAttention-style tiling keeps the score matrix on chip, so
 //    HBM traffic is linear in S and the kernel is bound by the matrix cores.
+//  * "Vector-Pipe Cost of the Softmax" / "Software Ordering of Matrix
+//    Instructions": in FP8 the softmax needs about as many vector cycles as the
+//    matrix products need matrix cycles, and only the instruction order overlaps
+//    the two, so the loop below is software-pipelined and its schedule is fixed
+//    with scheduling-group barriers.
 //  * "Precision and Underflow of FP8 Probabilities" and "Per-Block Scaling and
 //    Normalization by the Rounded Row Sum": probabilities of each (query row,
 //    64-key block) are multiplied by a power of two that puts the block maximum in
 //    [1, 2) before rounding to e4m3; the scaled FP8 matrix instruction divides it
 //    back out; each row is normalised by the sum of exactly the rounded values
-//    that multiply V.
+//    that multiply V, computed by one more matrix instruction.
 //  * "Lean P": probabilities are formed in base 2, p = 2^x with x the score minus
-//    the row maximum in base-2 units (this kernel evaluates 2^x exactly with the
-//    hardware exponential and rounds it to e4m3 - the page's "exact P").
+//    the row maximum in base-2 units (this kernel evaluates 2^x with the hardware
+//    exponential and rounds it to e4m3 - the page's "exact P").
 //
-// Work decomposition (one workgroup = 4 waves = 128 query rows of one head):
+// Work decomposition (one workgroup = 4 waves = 128 query rows of one head, two
+// workgroups per CU):
 //  * Each wave owns 32 query rows and computes S^T = K Q^T on 32x32 MFMA tiles,
 //    so every lane holds the scores of one query row (lane % 32) for half of the
 //    keys of a tile; row maxima need one lane-half exchange (v_permlane32_swap).
-//  * K and V tiles of 64 keys are staged through LDS (double buffered, padded rows)
-//    with coalesced 16-byte global loads; K is read back in MFMA operand layout,
-//    V with the LDS transpose read so that keys land along the reduction axis.
+//  * K and V tiles of 64 keys are staged through LDS rings of two buffers each,
+//    with coalesced 16-byte global loads issued two tiles ahead. K is read back in
+//    MFMA operand layout; V with the LDS transpose read so that keys land along the
+//    reduction axis. Row pitches (and, for FP8, a swap of key bits 2 and 3 in the
+//    V row order) make every LDS read of a half-wave hit 64 distinct banks.
 //  * O^T = V^T P^T accumulates on the MFMA with each lane owning one query row, so
 //    rescaling O by a per-row factor is a per-lane multiply.
-//  * The running maximum used as the exponent reference is updated lazily: O and
-//    the row sum are rescaled only when a row's maximum grows by more than
-//    kLazyThreshold binades (the per-block power of two keeps FP8 probabilities in
-//    range regardless, and float32 accumulators have ample headroom).
-//  * Causal-block skipping: a wave visits key tiles 0 .. (its last row) / 64 only;
-//    the mask is evaluated on the tile that straddles the diagonal.
+//  * Pipeline per 64-key tile t: QK for tile t+1 is issued while the probabilities
+//    of tile t are formed; BF16 then multiplies P_t V_t, FP8 multiplies P_{t-1}
+//    V_{t-1} (one stage later, so that the matrix work of one iteration - 4 QK, 4
+//    PV and 1 row-sum instructions - overlaps all of the vector work); the row
+//    maxima of tile t+1 close the iteration.
+//  * The exponent reference m_ref is an integer that is raised lazily: only when a
+//    row's maximum exceeds it by more than kLazyThreshold binades are O and the row
+//    sum rescaled (by a power of two; for FP8 the in-flight probabilities of the
+//    previous tile are re-scaled exactly through their E8M0 scale).
+//  * Causal-block skipping: a workgroup visits key tiles 0 .. (its last row) / 64;
+//    the mask is evaluated only on tiles that reach past a wave's first row.
 //  * Scheduling: workgroups are issued heaviest (last query tile) first; within a
 //    round over heads, consecutive workgroup ids (which the hardware spreads over
 //    the 8 XCDs) are mapped so that each XCD serves a contiguous range of heads,
 //    and query heads sharing a key/value head hit the same L2.
 #include <math.h>
+
+#include <type_traits>
 
 #include "device.h"
 #include "launch.h"
@@ -51,13 +66,19 @@ struct Cfg {
   static constexpr int ESZ = FP8 ? 1 : 2;
   static constexpr int KROW = DQK * ESZ;  // bytes of one K row
   static constexpr int VROW = DV * ESZ;
-  static constexpr int KPITCH = KROW + 16;  // padded LDS row pitch: 16 consecutive rows hit distinct banks
-  static constexpr int VPITCH = VROW + 16;
-  static constexpr int KTILE = BN * KPITCH;
-  static constexpr int VTILE = BN * VPITCH;
-  static constexpr int STAGE = KTILE + VTILE;
-  static constexpr int LDS_BYTES = 2 * STAGE;
-  static constexpr int KCHUNKS = BN * KROW / 16 / THREADS;  // 16-byte global loads per thread per tile
+  // LDS tiles are stored as column blocks of 64 bytes: block c holds bytes [64c, 64c+64)
+  // of every row, 16-byte chunk j of row r at chunk j ^ x(r) within the row's 64 bytes.
+  // K (x = (r >> 2) & 3): the 16-byte operand reads of 16 consecutive rows hit 16
+  // distinct 4-bank groups. V: FP8 rows are stored in key order with bits 2 and 3
+  // swapped and x = 2 ((r >> 2) & 1), so each half-wave transpose read (8 consecutive
+  // rows x 2 chunks) hits distinct banks; BF16 transpose reads (4 consecutive rows x
+  // 4 chunks) need no swizzle. No padding, so tiles can be filled by direct
+  // global-to-LDS loads, one contiguous 1 KiB run per wave instruction.
+  static constexpr int KBLK = BN * 64;  // bytes of one column block
+  static constexpr int KBUF = BN * KROW;
+  static constexpr int VBUF = BN * VROW;
+  static constexpr int LDS_BYTES = 2 * KBUF + 2 * VBUF;
+  static constexpr int KCHUNKS = BN * KROW / 16 / THREADS;  // 16-byte loads per thread per tile
   static constexpr int VCHUNKS = BN * VROW / 16 / THREADS;
   static constexpr int KSTEP = FP8 ? 64 : 16;  // MFMA reduction depth
   static constexpr int NKS = DQK / KSTEP;
@@ -74,17 +95,24 @@ struct AttnParams {
   const float* v_scale;
   uint16_t* o;
   float* lse;
-  int B, Hq, Hkv, S, nb, scale_block, n_qtiles;
+  int B, Hq, Hkv, S, nb, scale_shift, n_qtiles;  // scale block = 1 << scale_shift tokens
   float scale_log2;  // softmax_scale * log2(e)
 };
 
 template <bool FP8>
 using QOp = typename std::conditional<FP8, v8i, v8bf>::type;
 
+// LDS row of key k within an FP8 V tile: key bits 2 and 3 swapped, so that the 8 keys
+// one 16-lane group reads with a transpose load ({0-3, 8-11} or {4-7, 12-15} within a
+// 16-key run) occupy 8 consecutive rows.
+__device__ __forceinline__ int fp8_vrow(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
 template <bool FP8, int DQK>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   using C = Cfg<FP8, DQK>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  char* const kring = smem;                // [2 buffers][column blocks][BN rows][64 bytes]
+  char* const vring = smem + 2 * C::KBUF;  // same layout for V
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -107,15 +135,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
 
   const int q0_wg = qt * C::BM;
   const int q0 = q0_wg + wave * 32;
-  const int n_tiles = (min(q0_wg + C::BM, S) - 1) / C::BN + 1;
-  const bool wave_active = q0 < S;
-  const int n_tiles_w = wave_active ? (min(q0 + 32, S) - 1) / C::BN + 1 : 0;
+  // every wave runs the workgroup's trip count; tiles past a wave's rows are fully masked
+  const int n = (min(q0_wg + C::BM, S) - 1) / C::BN + 1;
   const int my_q = q0 + l32;
 
   const size_t bh_q = (size_t)(b * p.Hq + hq);
   const size_t bh_kv = (size_t)(b * p.Hkv + hkv);
   const char* kbase = p.k + bh_kv * S * C::KROW;
   const char* vbase = p.v + bh_kv * S * C::VROW;
+  const float* kscale = p.k_scale + bh_kv * p.nb;
+  const float* vscale = p.v_scale + bh_kv * p.nb;
 
   // ---- Q operand (B of S^T = K Q^T): lane holds Q[my_q][c*KSTEP + h*KSTEP/2 ...] ----
   QOp<FP8> qreg[C::NKS];
@@ -133,235 +162,459 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
       }
     }
   }
+  float c_q = p.scale_log2;  // multiplies raw scores into base-2 units (times the tile's k scale for FP8)
+  if constexpr (FP8) c_q *= p.q_scale[bh_q * p.nb + (min(q0, S - 1) >> p.scale_shift)];
 
-  float q_scale = 1.0f;
-  if constexpr (FP8) q_scale = p.q_scale[bh_q * p.nb + min(q0, S - 1) / p.scale_block];
-
-  // ---- global -> register -> LDS staging of K and V tiles ----
-  v4i kst[C::KCHUNKS];
-  v4i vst[C::VCHUNKS];
-  auto gload = [&](int t) {
-    const int kt = t * C::BN;
+  // ---- direct global -> LDS staging ----
+  // 16-byte position pos of a buffer is (column block, row r, stored chunk); the lane
+  // that fills it fetches the global chunk stored there. Each wave instruction fills 64
+  // consecutive positions (1 KiB), lane l at position base + l.
+  auto fill_k = [&](int t, int buf) {
+    char* dst = kring + buf * C::KBUF;
 #pragma unroll
     for (int i = 0; i < C::KCHUNKS; ++i) {
-      const int c = tid + i * C::THREADS;
-      const int row = c / (C::KROW / 16);
-      const int col = c % (C::KROW / 16);
-      const int gr = min(kt + row, S - 1);
-      kst[i] = *(const v4i*)(kbase + (size_t)gr * C::KROW + col * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < C::VCHUNKS; ++i) {
-      const int c = tid + i * C::THREADS;
-      const int row = c / (C::VROW / 16);
-      const int col = c % (C::VROW / 16);
-      const int gr = min(kt + row, S - 1);
-      vst[i] = *(const v4i*)(vbase + (size_t)gr * C::VROW + col * 16);
+      const int pos = tid + i * C::THREADS;
+      const int r = (pos >> 2) % C::BN;
+      const int j = (pos & 3) ^ ((r >> 2) & 3);
+      const int gr = min(t * C::BN + r, S - 1);
+      const char* src = kbase + (size_t)gr * C::KROW + (pos / (4 * C::BN)) * 64 + j * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + (i * C::THREADS + wave * 64) * 16), 16, 0, 0);
     }
   };
-  auto lstore = [&](int buf) {
-    char* ks = smem + buf * C::STAGE;
-    char* vs = ks + C::KTILE;
-#pragma unroll
-    for (int i = 0; i < C::KCHUNKS; ++i) {
-      const int c = tid + i * C::THREADS;
-      *(v4i*)(ks + (c / (C::KROW / 16)) * C::KPITCH + (c % (C::KROW / 16)) * 16) = kst[i];
-    }
+  auto fill_v = [&](int t, int buf) {
+    char* dst = vring + buf * C::VBUF;
 #pragma unroll
     for (int i = 0; i < C::VCHUNKS; ++i) {
-      const int c = tid + i * C::THREADS;
-      *(v4i*)(vs + (c / (C::VROW / 16)) * C::VPITCH + (c % (C::VROW / 16)) * 16) = vst[i];
+      const int pos = tid + i * C::THREADS;
+      const int r = (pos >> 2) % C::BN;
+      const int j = FP8 ? ((pos & 3) ^ (2 * ((r >> 2) & 1))) : (pos & 3);
+      const int gr = min(t * C::BN + (FP8 ? fp8_vrow(r) : r), S - 1);
+      const char* src = vbase + (size_t)gr * C::VROW + (pos / (4 * C::BN)) * 64 + j * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + (i * C::THREADS + wave * 64) * 16), 16, 0, 0);
     }
   };
+  // make this wave's direct loads visible before the barrier that publishes them
+  auto wait_fills = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
-  // ---- per-row state (each lane owns query row my_q) ----
-  v16f oacc[4];
+  // ---- per-lane LDS read offsets (the rest of each address is an immediate) ----
+  const int xk = (l32 >> 2) & 3;
+  int k_off0, k_off1;  // FP8: chunks 2h, 2h+1 of block c; BF16: chunk h (c even), 2+h (c odd) of block c/2
+  if constexpr (FP8) {
+    k_off0 = l32 * 64 + 16 * ((2 * h) ^ xk);
+    k_off1 = l32 * 64 + 16 * ((2 * h + 1) ^ xk);
+  } else {
+    k_off0 = l32 * 64 + 16 * (h ^ xk);
+    k_off1 = l32 * 64 + 16 * ((2 + h) ^ xk);
+  }
+  const int g1 = (lane >> 4) & 1;
+  int v_off0, v_off1;  // FP8: dv block halves 0 / 1 of a 64-byte column block
+  if constexpr (FP8) {
+    const int r8 = (lane & 15) >> 1;
+    const int xv = 2 * ((r8 >> 2) & 1);
+    v_off0 = (8 * h + r8) * 64 + 16 * (g1 ^ xv) + 8 * (lane & 1);
+    v_off1 = (8 * h + r8) * 64 + 16 * ((2 + g1) ^ xv) + 8 * (lane & 1);
+  } else {
+    v_off0 = (4 * h + ((lane & 15) >> 2)) * 64 + 32 * g1 + 8 * (lane & 3);
+    v_off1 = v_off0;
+  }
+
+  // S^T[key][query] of a tile, keys 32g + 8(r/4) + 4h + r%4 (registers r of sacc[g])
+  auto qk = [&](int buf, v16f (&s)[2]) {
+    const char* kb = kring + buf * C::KBUF;
 #pragma unroll
-  for (int d = 0; d < 4; ++d) oacc[d] = v16f{0};
-  float m_ref = -INFINITY;  // exponent reference (base-2 units)
-  float l_sum = 0.0f;       // row sum in units of 2^m_ref
-  const int k127 = opaque(kE8M0One);
-  const v8i ones_fp8 = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                        0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    if (t + 1 < n_tiles) gload(t + 1);
-
-    if (t < n_tiles_w) {
-      const char* ks = smem + (t & 1) * C::STAGE;
-      const char* vs = ks + C::KTILE;
-      const int kt = t * C::BN;
-
-      // S^T[key][query] for keys kt + 32g + (8(r/4) + 4h + r%4)
-      v16f sacc[2];
+    for (int g = 0; g < 2; ++g) {
+      s[g] = v16f{0};
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        sacc[g] = v16f{0};
-        const char* krow = ks + (32 * g + l32) * C::KPITCH + h * (C::KSTEP / 2) * C::ESZ;
-#pragma unroll
-        for (int c = 0; c < C::NKS; ++c) {
-          const char* src = krow + c * C::KSTEP * C::ESZ;
-          if constexpr (FP8) {
-            v4i lo = *(const v4i*)src;
-            v4i hi = *(const v4i*)(src + 16);
-            v8i a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            sacc[g] = mfma_fp8(a, qreg[c], sacc[g]);
-          } else {
-            v8bf a = *(const v8bf*)src;
-            sacc[g] = mfma_bf16(a, qreg[c], sacc[g]);
-          }
+      for (int c = 0; c < C::NKS; ++c) {
+        if constexpr (FP8) {
+          const char* blk = kb + c * C::KBLK + 32 * g * 64;
+          const v4i lo = *(const v4i*)(blk + k_off0);
+          const v4i hi = *(const v4i*)(blk + k_off1);
+          const v8i a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          s[g] = mfma_fp8(a, qreg[c], s[g]);
+        } else {
+          const char* blk = kb + (c >> 1) * C::KBLK + 32 * g * 64;
+          s[g] = mfma_bf16(*(const v8bf*)(blk + ((c & 1) ? k_off1 : k_off0)), qreg[c], s[g]);
         }
       }
-
-      // causal mask on the tile that reaches past the wave's first row
-      if (kt + C::BN - 1 > q0) {
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt + 32 * g + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (key > my_q) sacc[g][r] = -INFINITY;
-          }
-      }
-
-      // row maximum over the 64 keys of the tile
-      float bm = -INFINITY;
+    }
+  };
+  auto mask = [&](v16f (&s)[2], int t) {
+    const int kt = t * C::BN;
+    if (kt + C::BN - 1 > q0) {
 #pragma unroll
       for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) bm = fmaxf(bm, sacc[g][r]);
-      bm = max_across_halves(bm);
-
-      float c_log2 = p.scale_log2;
-      float k_scale = 1.0f, v_scale = 1.0f;
-      if constexpr (FP8) {
-        const size_t si = bh_kv * p.nb + kt / p.scale_block;
-        k_scale = p.k_scale[si];
-        v_scale = p.v_scale[si];
-        c_log2 = p.scale_log2 * q_scale * k_scale;
-      }
-      const float xmax = bm * c_log2;  // every visited tile has an unmasked key per row: finite
-
-      // lazy update of the exponent reference; a row's result depends on its own
-      // scores only (rows that do not need a new reference keep theirs: alpha = 1)
-      const bool grow = xmax > m_ref + kLazyThreshold;
-      if (__any(grow)) {
-        const float m_new = grow ? xmax : m_ref;
-        const float alpha = fast_exp2(m_ref - m_new);  // 0 on the first tile
+        for (int r = 0; r < 16; ++r)
+          if (kt + 32 * g + 8 * (r >> 2) + 4 * h + (r & 3) > my_q) s[g][r] = -INFINITY;
+    }
+  };
+  auto rowmax = [&](const v16f (&s)[2]) {
+    float m0 = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) oacc[d] *= alpha;
-        l_sum *= alpha;
+    for (int r = 1; r < 16; ++r) m0 = fmaxf(fmaxf(m0, s[0][r]), s[1][r]);
+    return max_across_halves(m0);
+  };
+
+  v16f oacc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) oacc[d] = v16f{0};
+
+  // ---- prologue: K0, V0, K1 resident; scores and maxima of tile 0 ----
+  fill_k(0, 0);
+  fill_v(0, 0);
+  if (n > 1) fill_k(1, 1);
+  if constexpr (FP8) {
+    // the PV stage of the first iteration multiplies an all-zero P with V buffer 1:
+    // make that buffer finite
+#pragma unroll
+    for (int i = 0; i < C::VCHUNKS; ++i) *(v4i*)(vring + C::VBUF + (tid + i * C::THREADS) * 16) = v4i{0, 0, 0, 0};
+  }
+  wait_fills();
+  __syncthreads();
+
+  // iterations t < n_steady need no causal mask on tile t+1 in any wave and prefetch
+  // K_{t+2}: their bodies are branch-free and carry a fixed instruction schedule
+  const int n_steady = max(0, min(n - 2, (q0_wg + 1) / C::BN - 1)) & ~1;
+
+  v16f sa[2], sb[2];
+  qk(0, sa);
+  mask(sa, 0);
+  float c_cur = c_q;
+  if constexpr (FP8) c_cur *= kscale[0];
+  float xmax0 = rowmax(sa) * c_cur;  // tile 0 always holds key 0 <= every row: finite
+  float m_ref = ceilf(xmax0);
+  bool rescale = false;
+  float alpha = 1.0f;
+
+  // epilogue: O / l as bfloat16, and the log-sum-exp
+  auto store_out = [&](float l_sum) {
+    if (q0 >= S || my_q >= S) return;
+    const float inv_l = 1.0f / l_sum;
+    uint16_t* orow = p.o + (bh_q * S + my_q) * C::DV;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        uint2 w;
+        w.x = pack_bf16x2(oacc[d][4 * r4 + 0] * inv_l, oacc[d][4 * r4 + 1] * inv_l);
+        w.y = pack_bf16x2(oacc[d][4 * r4 + 2] * inv_l, oacc[d][4 * r4 + 3] * inv_l);
+        *(uint2*)(orow + 32 * d + 8 * r4 + 4 * h) = w;
+      }
+    if (p.lse != nullptr && h == 0) p.lse[bh_q * S + my_q] = kLn2 * (m_ref + log2f(l_sum));
+  };
+
+  if constexpr (FP8) {
+    // ===================== FP8: three-stage pipeline =====================
+    const v8i ones_fp8 = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                          0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+    const int k127 = opaque(kE8M0One);
+
+    // V scale = rv * 2^ev, rv in [1, 2): 2^ev is the V operand's E8M0 scale (exact);
+    // rv is 1 for power-of-two scales (as zyfa_quantize_fp8 writes them). O is kept in
+    // units of 1 / rv of the last tile added, and rescaled by the ratio when rv changes.
+    v16f rs_acc = v16f{0};  // rounded row sum, accumulated on the MFMA (any register holds it)
+    float rv_o = 1.0f;      // O holds sum(w v) / rv_o
+
+    auto vsplit = [&](int t, float& rv, int& sv) {
+      int ev;
+      rv = 2.0f * frexpf(vscale[(t * C::BN) >> p.scale_shift], &ev);
+      sv = kE8M0One + ev - 1;
+    };
+    auto block_exp = [&](float xmax) { return (int)fmaxf(floorf(xmax - m_ref), -126.0f); };
+
+    float rv_cur;
+    int sv_cur;
+    vsplit(0, rv_cur, sv_cur);
+    int eb_cur = block_exp(xmax0);
+
+    v8i pa = v8i{0}, pb = v8i{0};
+    int sp_prev = kE8M0One, sv_prev = kE8M0One;
+    float rv_prev = 1.0f;
+    int la = 0;
+
+    // bring O and the row sum to the units of the P about to be added: the reference
+    // change (alpha, a power of two; the in-flight P gets it through its E8M0 scale) and
+    // the V-scale mantissa ratio. Both are rare: the branch is uniform per wave.
+    auto fix_units = [&]() {
+      if (rescale || rv_prev != rv_o) {
+        const float f = (rescale ? alpha : 1.0f) * (rv_o / rv_prev);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) oacc[d] *= f;
+        if (rescale) {
+          rs_acc[0] *= alpha;
+          sp_prev = max(sp_prev + la, 0);
+        }
+        rv_o = rv_prev;
+        rescale = false;
+      }
+    };
+
+    // O^T += V^T P^T and the rounded row sum, for the tile whose P is pp
+    auto pv = [&](const v8i& pp, int sp, int sv, int vbuf) {
+      const char* vb = vring + vbuf * C::VBUF;
+      const int svr = opaque(sv);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        int va[8];
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const char* src = vb + (d >> 1) * C::KBLK + 16 * qd * 64 + ((d & 1) ? v_off1 : v_off0);
+          v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)src);
+          va[2 * qd] = x[0];
+          va[2 * qd + 1] = x[1];
+        }
+        const v8i a = {va[0], va[1], va[2], va[3], va[4], va[5], va[6], va[7]};
+        oacc[d] = mfma_fp8_scaled(a, pp, oacc[d], svr, sp);
+      }
+      rs_acc = mfma_fp8_scaled(ones_fp8, pp, rs_acc, k127, sp);
+    };
+
+    // One iteration t: prefetch K_{t+2}; QK of tile t+1; PV of tile t-1; P of tile t;
+    // maxima of tile t+1. STEADY iterations (t + 2 < n, no mask) have no branches
+    // between the rare unit fix at the top and the rare reference update at the end.
+    auto step = [&](auto steady_tag, int t, v16f (&s_cur)[2], v16f (&s_next)[2], v8i& p_prev, v8i& p_cur) {
+      constexpr bool STEADY = decltype(steady_tag)::value;
+      const bool has_next = STEADY || t + 1 < n;
+      fix_units();
+      if (STEADY || t + 2 < n) fill_k(t + 2, t & 1);
+      if (has_next) qk((t + 1) & 1, s_next);
+      pv(p_prev, sp_prev, sv_prev, (t + 1) & 1);
+
+      // p = 2^(s*c - m_ref - eb): the block maximum lands in [1, 2), rounded to e4m3
+      const float bias = m_ref + (float)eb_cur;
+      int pw[8];
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float p0 = fast_exp2(fmaf(s_cur[g][4 * w + 0], c_cur, -bias));
+          const float p1 = fast_exp2(fmaf(s_cur[g][4 * w + 1], c_cur, -bias));
+          const float p2 = fast_exp2(fmaf(s_cur[g][4 * w + 2], c_cur, -bias));
+          const float p3 = fast_exp2(fmaf(s_cur[g][4 * w + 3], c_cur, -bias));
+          pw[4 * g + w] = cvt_pk_fp8<true>(p2, p3, cvt_pk_fp8<false>(p0, p1, 0));
+        }
+      p_cur = v8i{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+      sp_prev = kE8M0One + eb_cur;
+      sv_prev = sv_cur;
+      rv_prev = rv_cur;
+
+      float xmax = 0.0f, c_next = c_cur;
+      if (has_next) {
+        if constexpr (!STEADY) mask(s_next, t + 1);
+        c_next = c_q * kscale[((t + 1) * C::BN) >> p.scale_shift];
+        xmax = rowmax(s_next) * c_next;
+      }
+      if (has_next) {
+        // lazy reference update, branch-free: rows that do not grow keep m_ref (alpha = 1)
+        const bool grow = xmax > m_ref + kLazyThreshold;
+        rescale = __any(grow);
+        const float m_new = grow ? ceilf(xmax) : m_ref;
+        la = (int)(m_ref - m_new);
+        alpha = fast_exp2((float)la);
         m_ref = m_new;
+        vsplit(t + 1, rv_cur, sv_cur);
+        eb_cur = block_exp(xmax);
+        c_cur = c_next;
       }
+      wait_fills();
+      __syncthreads();
+      if (has_next) fill_v(t + 1, (t + 1) & 1);
+    };
 
-      if constexpr (FP8) {
-        // block power of two: 2^-eb puts the block maximum of this row in [1, 2)
-        const int eb = max((int)floorf(xmax - m_ref), -126);
-        // V scale = rv * 2^ev with rv in [1, 2): 2^ev goes to the V operand's E8M0
-        // scale, rv is folded into the probabilities before rounding
-        int ev;
-        const float rv = 2.0f * frexpf(v_scale, &ev);
-        ev -= 1;
-        const float bias = m_ref + (float)eb - __builtin_amdgcn_logf(rv);
-        int pw[8];
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const float p0 = fast_exp2(fmaf(sacc[g][4 * w + 0], c_log2, -bias));
-            const float p1 = fast_exp2(fmaf(sacc[g][4 * w + 1], c_log2, -bias));
-            const float p2 = fast_exp2(fmaf(sacc[g][4 * w + 2], c_log2, -bias));
-            const float p3 = fast_exp2(fmaf(sacc[g][4 * w + 3], c_log2, -bias));
-            int word = cvt_pk_fp8<false>(p0, p1, 0);
-            pw[4 * g + w] = cvt_pk_fp8<true>(p2, p3, word);
-          }
-        const v8i pv = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
-        const int scale_p = kE8M0One + eb;
-        const int scale_v = opaque(kE8M0One + ev);
-
-        // O^T[dv][query] += V^T P^T; V^T operand via LDS transpose reads:
-        // byte j of a lane's operand is key 32(j/16) + 8((j%16)/4) + 4h + j%4,
-        // the same key order as the probability bytes.
-        const int r8 = (lane & 15) >> 1;
-        const int colbase = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          int va[8];
+    // Steady iteration, hand-ordered: slot i issues matrix instruction i (QK of tile t+1,
+    // then PV and the row sum of tile t-1), fetches the LDS operands of instruction i+2,
+    // and runs one 64-cycle share of the vector work (4 exponentials and 2 conversions of
+    // tile t's probabilities, or the maxima of tile t+1 once its scores are complete).
+    // sched_barrier keeps each slot's instructions in place.
+    auto steady_step = [&](int t, v16f (&s_cur)[2], v16f (&s_next)[2], v8i& p_prev, v8i& p_cur) {
+      constexpr int NQK = 2 * C::NKS;
+      constexpr int NSLOT = NQK + 5;
+      fix_units();
+      const char* kb = kring + ((t + 1) & 1) * C::KBUF;
+      const char* vb = vring + ((t + 1) & 1) * C::VBUF;  // V of tile t-1
+      const float bias = m_ref + (float)eb_cur;
+      const int svr = opaque(sv_prev);
+      const int sp = sp_prev;
+      v8i op[3];
+      auto read_op = [&](int i, v8i& dst) {
+        if (i < NQK) {
+          const char* blk = kb + (i >> 1) * C::KBLK + 32 * (i & 1) * 64;
+          const v4i lo = *(const v4i*)(blk + k_off0);
+          const v4i hi = *(const v4i*)(blk + k_off1);
+          dst = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else if (i < NQK + 4) {
+          const int d = i - NQK;
 #pragma unroll
           for (int qd = 0; qd < 4; ++qd) {
-            const int key = 32 * (qd >> 1) + 16 * (qd & 1) + 8 * (r8 >> 2) + 4 * h + (r8 & 3);
-            const char* src = vs + key * C::VPITCH + 32 * d + colbase;
-            v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)src);
-            va[2 * qd] = x[0];
-            va[2 * qd + 1] = x[1];
+            const char* src = vb + (d >> 1) * C::KBLK + 16 * qd * 64 + ((d & 1) ? v_off1 : v_off0);
+            const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)src);
+            dst[2 * qd] = x[0];
+            dst[2 * qd + 1] = x[1];
           }
-          const v8i a = {va[0], va[1], va[2], va[3], va[4], va[5], va[6], va[7]};
-          oacc[d] = mfma_fp8_scaled(a, pv, oacc[d], scale_v, scale_p);
         }
-        // rounded row sum: the same probability bytes and scales, against a ones matrix
-        const v16f rs = mfma_fp8_scaled(ones_fp8, pv, v16f{0}, k127, scale_p);
-        l_sum = fmaf(rs[0], 1.0f / rv, l_sum);
-      } else {
-        // BF16: p = 2^(x - m_ref) rounded to bf16 for P V; row sum in float32
-        float part = 0.0f;
-        v8bf pb[4];
+      };
+      read_op(0, op[0]);
+      read_op(1, op[1]);
+      fill_k(t + 2, t & 1);
+      s_next[0] = v16f{0};
+      s_next[1] = v16f{0};
+      float mx = -INFINITY;
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const int g = tt >> 1;
-          const int r0 = 8 * (tt & 1);
-          float pr[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            pr[j] = fast_exp2(fmaf(sacc[g][r0 + j], c_log2, -m_ref));
-            part += pr[j];
-          }
-#pragma unroll
-          for (int j = 0; j < 8; ++j) pb[tt][j] = (__bf16)pr[j];
+      for (int i = 0; i < NSLOT; ++i) {
+        if (i < NQK)
+          s_next[i & 1] = mfma_fp8(op[i % 3], qreg[i >> 1], s_next[i & 1]);
+        else if (i < NQK + 4)
+          oacc[i - NQK] = mfma_fp8_scaled(op[i % 3], p_prev, oacc[i - NQK], svr, sp);
+        else
+          rs_acc = mfma_fp8_scaled(ones_fp8, p_prev, rs_acc, k127, sp);
+        if (i + 2 < NSLOT) read_op(i + 2, op[(i + 2) % 3]);
+        if (i < 8) {
+          const int g = i >> 2, w = i & 3;
+          const float p0 = fast_exp2(fmaf(s_cur[g][4 * w + 0], c_cur, -bias));
+          const float p1 = fast_exp2(fmaf(s_cur[g][4 * w + 1], c_cur, -bias));
+          const float p2 = fast_exp2(fmaf(s_cur[g][4 * w + 2], c_cur, -bias));
+          const float p3 = fast_exp2(fmaf(s_cur[g][4 * w + 3], c_cur, -bias));
+          p_cur[i] = cvt_pk_fp8<true>(p2, p3, cvt_pk_fp8<false>(p0, p1, 0));
         }
-        l_sum += part;
-        const int r4 = (lane & 15) >> 2;
-        const int colbase = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        if (i >= NQK + 1 && i >= 6) {  // the scores of tile t+1 are complete: row maxima
+          const int r0 = i == NSLOT - 3 ? 0 : (i == NSLOT - 2 ? 6 : 11);
+          const int r1 = i == NSLOT - 3 ? 6 : (i == NSLOT - 2 ? 11 : 16);
+          if (i >= NSLOT - 3) {
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            const int key0 = 32 * (tt >> 1) + 16 * (tt & 1) + 4 * h + r4;
-            const char* src0 = vs + key0 * C::VPITCH + (32 * d + colbase) * 2;
-            const char* src1 = src0 + 8 * C::VPITCH;
-            const v4bf x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)src0);
-            const v4bf x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)src1);
-            const v8bf a = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-            oacc[d] = mfma_bf16(a, pb[tt], oacc[d]);
+            for (int r = r0; r < r1; ++r) mx = fmaxf(fmaxf(mx, s_next[0][r]), s_next[1][r]);
           }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sp_prev = kE8M0One + eb_cur;
+      sv_prev = sv_cur;
+      rv_prev = rv_cur;
+
+      const float c_next = c_q * kscale[((t + 1) * C::BN) >> p.scale_shift];
+      const float xmax = max_across_halves(mx) * c_next;
+      const bool grow = xmax > m_ref + kLazyThreshold;
+      rescale = __any(grow);
+      const float m_new = grow ? ceilf(xmax) : m_ref;
+      la = (int)(m_ref - m_new);
+      alpha = fast_exp2((float)la);
+      m_ref = m_new;
+      vsplit(t + 1, rv_cur, sv_cur);
+      eb_cur = block_exp(xmax);
+      c_cur = c_next;
+      wait_fills();
+      __syncthreads();
+      fill_v(t + 1, (t + 1) & 1);
+    };
+
+    int t = 0;
+    for (; t < n_steady; t += 2) {
+      steady_step(t, sa, sb, pa, pb);
+      steady_step(t + 1, sb, sa, pb, pa);
+    }
+    for (; t < n; t += 2) {
+      step(std::false_type{}, t, sa, sb, pa, pb);
+      if (t + 1 < n) step(std::false_type{}, t + 1, sb, sa, pb, pa);
+    }
+    // drain: PV of the last tile (its P is pb if n - 1 is even, else pa)
+    fix_units();
+    pv(((n - 1) & 1) ? pa : pb, sp_prev, sv_prev, (n - 1) & 1);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) pin_acc(oacc[d]);
+    pin_acc(rs_acc);
+    // O = oacc * rv_o / l
+    store_out(rs_acc[0] / rv_o);
+  } else {
+    // ===================== BF16: two-stage pipeline =====================
+    float l_part = 0.0f;  // this lane's half of the row sum (float32, unrounded p)
+
+    // One iteration t: prefetch K_{t+2}, V_{t+1}; QK of tile t+1; P and PV of tile t;
+    // maxima of tile t+1.
+    auto step = [&](auto steady_tag, int t, v16f (&s_cur)[2], v16f (&s_next)[2]) {
+      constexpr bool STEADY = decltype(steady_tag)::value;
+      const bool has_next = STEADY || t + 1 < n;
+      if (rescale) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) oacc[d] *= alpha;
+        l_part *= alpha;
+        rescale = false;
+      }
+      // K_{t+2} replaces K_t and V_{t+1} replaces V_{t-1}: both last read in the
+      // previous iteration
+      if (STEADY || t + 2 < n) fill_k(t + 2, t & 1);
+      if (has_next) fill_v(t + 1, (t + 1) & 1);
+      if (has_next) qk((t + 1) & 1, s_next);
+
+      // p = 2^(s*c - m_ref), rounded to bf16 for P V; float32 row sum
+      v8bf pbf[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int g = tt >> 1;
+        const int r0 = 8 * (tt & 1);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float pr = fast_exp2(fmaf(s_cur[g][r0 + j], c_cur, -m_ref));
+          l_part += pr;
+          pbf[tt][j] = (__bf16)pr;
         }
       }
-    }
+      // O^T += V^T P^T: keys of MFMA tt are 32(tt/2) + 16(tt%2) + 8u + 4h + r
+      {
+        const char* vb = vring + (t & 1) * C::VBUF + v_off0;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const char* src = vb + d * C::KBLK + (32 * (tt >> 1) + 16 * (tt & 1)) * 64;
+            const v4bf x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)src);
+            const v4bf x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(src + 8 * 64));
+            oacc[d] = mfma_bf16(__builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7), pbf[tt], oacc[d]);
+          }
+      }
+      float xmax = 0.0f;
+      if (has_next) {
+        if constexpr (!STEADY) mask(s_next, t + 1);
+        xmax = rowmax(s_next) * c_cur;
+      }
+      if (has_next) {
+        const bool grow = xmax > m_ref + kLazyThreshold;
+        rescale = __any(grow);
+        const float m_new = grow ? ceilf(xmax) : m_ref;
+        alpha = fast_exp2(m_ref - m_new);
+        m_ref = m_new;
+      }
+      if constexpr (STEADY) {
+        // 16 QK instructions while P is formed, then 16 PV instructions with the maxima
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
+      }
+      wait_fills();
+      __syncthreads();
+    };
 
-    if (t + 1 < n_tiles) lstore((t + 1) & 1);
-    __syncthreads();
+    int t = 0;
+    for (; t < n_steady; t += 2) {
+      step(std::true_type{}, t, sa, sb);
+      step(std::true_type{}, t + 1, sb, sa);
+    }
+    for (; t < n; t += 2) {
+      step(std::false_type{}, t, sa, sb);
+      if (t + 1 < n) step(std::false_type{}, t + 1, sb, sa);
+    }
+    store_out(sum_across_halves(l_part));
   }
-
-  if (!wave_active) return;
-  if constexpr (!FP8) l_sum = sum_across_halves(l_sum);
-  if (my_q >= S) return;
-
-  const float inv_l = 1.0f / l_sum;
-  uint16_t* orow = p.o + (bh_q * S + my_q) * C::DV;
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int dv = 32 * d + 8 * r4 + 4 * h;
-      uint2 w;
-      w.x = pack_bf16x2(oacc[d][4 * r4 + 0] * inv_l, oacc[d][4 * r4 + 1] * inv_l);
-      w.y = pack_bf16x2(oacc[d][4 * r4 + 2] * inv_l, oacc[d][4 * r4 + 3] * inv_l);
-      *(uint2*)(orow + dv) = w;
-    }
-  if (p.lse != nullptr && h == 0) p.lse[bh_q * S + my_q] = kLn2 * (m_ref + log2f(l_sum));
 }
 
 template <bool FP8, int DQK>
@@ -380,7 +633,7 @@ static hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   p.Hq = a.Hq;
   p.Hkv = a.Hkv;
   p.S = a.S;
-  p.scale_block = FP8 ? a.scale_block : 1;
+  p.scale_shift = FP8 ? (a.scale_block == 64 ? 6 : 7) : 0;
   p.nb = FP8 ? (a.S + a.scale_block - 1) / a.scale_block : 0;
   p.n_qtiles = (a.S + C::BM - 1) / C::BM;
   p.scale_log2 = a.softmax_scale * kLog2e;

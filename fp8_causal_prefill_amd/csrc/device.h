@@ -36,6 +36,7 @@ typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 typedef __attribute__((address_space(3))) v4bf lds_v4bf;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -62,6 +63,12 @@ __device__ __forceinline__ int opaque(int x) {
   asm volatile("" : "+v"(x));
   return x;
 }
+
+// Materialise a matrix accumulator here, in the current (uniform) control flow. A
+// matrix instruction reads its operands from all 64 lanes whatever EXEC holds, so it
+// must not be moved into a lane-divergent region (such as a guarded output store),
+// where operands built inside that region exist only in the active lanes.
+__device__ __forceinline__ void pin_acc(v16f& x) { asm volatile("" : "+v"(x)); }
 
 // max of a value across lanes i and i+32.
 __device__ __forceinline__ float max_across_halves(float x) {
