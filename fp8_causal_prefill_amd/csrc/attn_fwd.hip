@@ -316,16 +316,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
     v16f rs_acc = v16f{0};  // rounded row sum, accumulated on the MFMA (any register holds it)
     float rv_o = 1.0f;      // O holds sum(w v) / rv_o
 
-    auto vsplit = [&](int t, float& rv, int& sv) {
+    auto vsplit = [&](float vsc, float& rv, int& sv) {
       int ev;
-      rv = 2.0f * frexpf(vscale[(t * C::BN) >> p.scale_shift], &ev);
+      rv = 2.0f * frexpf(vsc, &ev);
       sv = kE8M0One + ev - 1;
     };
+    // K and V scales of tile t+1 while iteration t runs; the loads for tile t+2 are
+    // issued at the top of iteration t, ahead of the tile fills whose wait covers them
+    auto sidx = [&](int tile) { return min((tile * C::BN) >> p.scale_shift, p.nb - 1); };
+    float ks_next = kscale[sidx(1)];
+    float vs_next = vscale[sidx(1)];
     auto block_exp = [&](float xmax) { return (int)fmaxf(floorf(xmax - m_ref), -126.0f); };
 
     float rv_cur;
     int sv_cur;
-    vsplit(0, rv_cur, sv_cur);
+    vsplit(vscale[0], rv_cur, sv_cur);
     int eb_cur = block_exp(xmax0);
 
     v8i pa = v8i{0}, pb = v8i{0};
@@ -338,6 +343,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
     // the V-scale mantissa ratio. Both are rare: the branch is uniform per wave.
     auto fix_units = [&]() {
       if (rescale || rv_prev != rv_o) {
+        rare_branch();
         const float f = (rescale ? alpha : 1.0f) * (rv_o / rv_prev);
 #pragma unroll
         for (int d = 0; d < 4; ++d) oacc[d] *= f;
@@ -377,6 +383,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
       constexpr bool STEADY = decltype(steady_tag)::value;
       const bool has_next = STEADY || t + 1 < n;
       fix_units();
+      const float ks_pf = kscale[sidx(t + 2)];
+      const float vs_pf = vscale[sidx(t + 2)];
       if (STEADY || t + 2 < n) fill_k(t + 2, t & 1);
       if (has_next) qk((t + 1) & 1, s_next);
       pv(p_prev, sp_prev, sv_prev, (t + 1) & 1);
@@ -402,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
       float xmax = 0.0f, c_next = c_cur;
       if (has_next) {
         if constexpr (!STEADY) mask(s_next, t + 1);
-        c_next = c_q * kscale[((t + 1) * C::BN) >> p.scale_shift];
+        c_next = c_q * ks_next;
         xmax = rowmax(s_next) * c_next;
       }
       if (has_next) {
@@ -413,11 +421,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
         la = (int)(m_ref - m_new);
         alpha = fast_exp2((float)la);
         m_ref = m_new;
-        vsplit(t + 1, rv_cur, sv_cur);
+        vsplit(vs_next, rv_cur, sv_cur);
         eb_cur = block_exp(xmax);
         c_cur = c_next;
       }
       wait_fills();
+      ks_next = ks_pf;
+      vs_next = vs_pf;
       __syncthreads();
       if (has_next) fill_v(t + 1, (t + 1) & 1);
     };
@@ -454,6 +464,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
           }
         }
       };
+      const float ks_pf = kscale[sidx(t + 2)];
+      const float vs_pf = vscale[sidx(t + 2)];
       read_op(0, op[0]);
       read_op(1, op[1]);
       fill_k(t + 2, t & 1);
@@ -477,6 +489,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
           const float p2 = fast_exp2(fmaf(s_cur[g][4 * w + 2], c_cur, -bias));
           const float p3 = fast_exp2(fmaf(s_cur[g][4 * w + 3], c_cur, -bias));
           p_cur[i] = cvt_pk_fp8<true>(p2, p3, cvt_pk_fp8<false>(p0, p1, 0));
+          keep_here(p_cur[i]);
         }
         if (i >= NQK + 1 && i >= 6) {  // the scores of tile t+1 are complete: row maxima
           const int r0 = i == NSLOT - 3 ? 0 : (i == NSLOT - 2 ? 6 : 11);
@@ -488,11 +501,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      // the products of this iteration stay in its slots (the next iteration's unit fix
+      // is a branch, and the compiler would otherwise sink them past it)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) keep_here(oacc[d]);
+      keep_here(rs_acc);
       sp_prev = kE8M0One + eb_cur;
       sv_prev = sv_cur;
       rv_prev = rv_cur;
 
-      const float c_next = c_q * kscale[((t + 1) * C::BN) >> p.scale_shift];
+      const float c_next = c_q * ks_next;
       const float xmax = max_across_halves(mx) * c_next;
       const bool grow = xmax > m_ref + kLazyThreshold;
       rescale = __any(grow);
@@ -500,10 +518,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
       la = (int)(m_ref - m_new);
       alpha = fast_exp2((float)la);
       m_ref = m_new;
-      vsplit(t + 1, rv_cur, sv_cur);
+      vsplit(vs_next, rv_cur, sv_cur);
       eb_cur = block_exp(xmax);
       c_cur = c_next;
       wait_fills();
+      ks_next = ks_pf;
+      vs_next = vs_pf;
+      keep_here(ks_next);
+      keep_here(vs_next);
       __syncthreads();
       fill_v(t + 1, (t + 1) & 1);
     };
@@ -535,6 +557,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
       constexpr bool STEADY = decltype(steady_tag)::value;
       const bool has_next = STEADY || t + 1 < n;
       if (rescale) {
+        rare_branch();
 #pragma unroll
         for (int d = 0; d < 4; ++d) oacc[d] *= alpha;
         l_part *= alpha;

@@ -60,7 +60,9 @@ __device__ __forceinline__ v16f mfma_bf16(const v8bf& a, const v8bf& b, const v1
 // Keep a value in a VGPR so the compiler cannot fold it into an instruction constant
 // (scale operands of the scaled MFMA must come from registers).
 __device__ __forceinline__ int opaque(int x) {
+#if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("" : "+v"(x));
+#endif
   return x;
 }
 
@@ -68,7 +70,28 @@ __device__ __forceinline__ int opaque(int x) {
 // matrix instruction reads its operands from all 64 lanes whatever EXEC holds, so it
 // must not be moved into a lane-divergent region (such as a guarded output store),
 // where operands built inside that region exist only in the active lanes.
-__device__ __forceinline__ void pin_acc(v16f& x) { asm volatile("" : "+v"(x)); }
+//
+// The asm helpers below are compiled in the device pass only: the host pass does not
+// know VGPR constraints and would reject the kernels that use them.
+__device__ __forceinline__ void pin_acc(v16f& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(x));
+#endif
+}
+
+// An empty use of x at this point of the program. The instruction producing x can
+// then not be sunk below it (e.g. out of a software-pipeline slot into a later basic
+// block where x is consumed), which the compiler otherwise does to shorten live ranges.
+template <class T>
+__device__ __forceinline__ void keep_here(const T& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::"v"(x));
+#endif
+}
+
+// A side effect that stops the compiler from if-converting the rare branch it sits in
+// (speculating its body into unconditional vector work).
+__device__ __forceinline__ void rare_branch() { asm volatile(""); }
 
 // max of a value across lanes i and i+32.
 __device__ __forceinline__ float max_across_halves(float x) {
