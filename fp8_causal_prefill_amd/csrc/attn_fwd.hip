@@ -84,6 +84,7 @@ struct Cfg {
   static constexpr int NKS = DQK / KSTEP;
   static_assert(BN * KROW % (16 * THREADS) == 0 && BN * VROW % (16 * THREADS) == 0, "tile load split");
   static_assert(DQK % KSTEP == 0, "head dim must divide the MFMA depth");
+  static_assert(BM == 2 * BN, "steady iterations rely on two key tiles per query tile");
 };
 
 struct AttnParams {
@@ -168,33 +169,77 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   // ---- direct global -> LDS staging ----
   // 16-byte position pos of a buffer is (column block, row r, stored chunk); the lane
   // that fills it fetches the global chunk stored there. Each wave instruction fills 64
-  // consecutive positions (1 KiB), lane l at position base + l.
-  auto fill_k = [&](int t, int buf) {
-    char* dst = kring + buf * C::KBUF;
+  // consecutive positions (1 KiB), lane l at position base + l. A lane's source offset
+  // within a tile does not depend on the tile; only the last tile of a sequence whose
+  // length is not a multiple of BN clamps its rows to S - 1.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto k_pos_row = [&](int i) { return ((tid + i * C::THREADS) >> 2) % C::BN; };
+  auto k_pos_off = [&](int i) {  // bytes within the K row
+    const int pos = tid + i * C::THREADS;
+    const int r = (pos >> 2) % C::BN;
+    return (pos / (4 * C::BN)) * 64 + ((pos & 3) ^ ((r >> 2) & 3)) * 16;
+  };
+  auto v_pos_row = [&](int i) {  // key (row of the global tile) stored at this position
+    const int r = ((tid + i * C::THREADS) >> 2) % C::BN;
+    return FP8 ? fp8_vrow(r) : r;
+  };
+  auto v_pos_off = [&](int i) {
+    const int pos = tid + i * C::THREADS;
+    const int r = (pos >> 2) % C::BN;
+    return (pos / (4 * C::BN)) * 64 + (FP8 ? ((pos & 3) ^ (2 * ((r >> 2) & 1))) : (pos & 3)) * 16;
+  };
+  uint32_t k_src[C::KCHUNKS], v_src[C::VCHUNKS];
 #pragma unroll
-    for (int i = 0; i < C::KCHUNKS; ++i) {
-      const int pos = tid + i * C::THREADS;
-      const int r = (pos >> 2) % C::BN;
-      const int j = (pos & 3) ^ ((r >> 2) & 3);
-      const int gr = min(t * C::BN + r, S - 1);
-      const char* src = kbase + (size_t)gr * C::KROW + (pos / (4 * C::BN)) * 64 + j * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + (i * C::THREADS + wave * 64) * 16), 16, 0, 0);
+  for (int i = 0; i < C::KCHUNKS; ++i) k_src[i] = k_pos_row(i) * C::KROW + k_pos_off(i);
+#pragma unroll
+  for (int i = 0; i < C::VCHUNKS; ++i) v_src[i] = v_pos_row(i) * C::VROW + v_pos_off(i);
+  const uint32_t k_lds = lds_address(kring), v_lds = lds_address(vring);
+
+  auto fill_k = [&](int t, int buf) {
+    const int t0 = t * C::BN;
+    const uint32_t dst = k_lds + buf * C::KBUF + wave_u * 64 * 16;
+    if (t0 + C::BN <= S) {
+      const char* tile = kbase + (size_t)t0 * C::KROW;
+#pragma unroll
+      for (int i = 0; i < C::KCHUNKS; ++i) lds_copy16(tile, k_src[i], dst + i * C::THREADS * 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::KCHUNKS; ++i) {
+        const int gr = min(t0 + k_pos_row(i), S - 1);
+        lds_copy16(kbase + (size_t)gr * C::KROW + k_pos_off(i), dst + i * C::THREADS * 16);
+      }
     }
   };
   auto fill_v = [&](int t, int buf) {
-    char* dst = vring + buf * C::VBUF;
+    const int t0 = t * C::BN;
+    const uint32_t dst = v_lds + buf * C::VBUF + wave_u * 64 * 16;
+    if (t0 + C::BN <= S) {
+      const char* tile = vbase + (size_t)t0 * C::VROW;
 #pragma unroll
-    for (int i = 0; i < C::VCHUNKS; ++i) {
-      const int pos = tid + i * C::THREADS;
-      const int r = (pos >> 2) % C::BN;
-      const int j = FP8 ? ((pos & 3) ^ (2 * ((r >> 2) & 1))) : (pos & 3);
-      const int gr = min(t * C::BN + (FP8 ? fp8_vrow(r) : r), S - 1);
-      const char* src = vbase + (size_t)gr * C::VROW + (pos / (4 * C::BN)) * 64 + j * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + (i * C::THREADS + wave * 64) * 16), 16, 0, 0);
+      for (int i = 0; i < C::VCHUNKS; ++i) lds_copy16(tile, v_src[i], dst + i * C::THREADS * 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::VCHUNKS; ++i) {
+        const int gr = min(t0 + v_pos_row(i), S - 1);
+        lds_copy16(vbase + (size_t)gr * C::VROW + v_pos_off(i), dst + i * C::THREADS * 16);
+      }
     }
   };
-  // make this wave's direct loads visible before the barrier that publishes them
-  auto wait_fills = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  // the copies of full tiles, for iterations that only see full tiles (no branch)
+  auto fill_k_full = [&](int t, int buf) {
+    const char* tile = kbase + (size_t)(t * C::BN) * C::KROW;
+    const uint32_t dst = k_lds + buf * C::KBUF + wave_u * 64 * 16;
+#pragma unroll
+    for (int i = 0; i < C::KCHUNKS; ++i) lds_copy16(tile, k_src[i], dst + i * C::THREADS * 16);
+  };
+  auto fill_v_full = [&](int t, int buf) {
+    const char* tile = vbase + (size_t)(t * C::BN) * C::VROW;
+    const uint32_t dst = v_lds + buf * C::VBUF + wave_u * 64 * 16;
+#pragma unroll
+    for (int i = 0; i < C::VCHUNKS; ++i) lds_copy16(tile, v_src[i], dst + i * C::THREADS * 16);
+  };
+  // make this wave's copies complete before the barrier that publishes them
+  auto wait_fills = [] { wait_vmem(); };
 
   // ---- per-lane LDS read offsets (the rest of each address is an immediate) ----
   const int xk = (l32 >> 2) & 3;
@@ -274,7 +319,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   __syncthreads();
 
   // iterations t < n_steady need no causal mask on tile t+1 in any wave and prefetch
-  // K_{t+2}: their bodies are branch-free and carry a fixed instruction schedule
+  // K_{t+2}: their bodies are branch-free and carry a fixed instruction schedule. With
+  // BM = 2 BN and n_steady even, every tile they fetch (t + 2 <= (q0_wg + 1) / BN - 1)
+  // ends before row q0_wg < S: no clamping.
   const int n_steady = max(0, min(n - 2, (q0_wg + 1) / C::BN - 1)) & ~1;
 
   v16f sa[2], sb[2];
@@ -468,7 +515,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
       const float vs_pf = vscale[sidx(t + 2)];
       read_op(0, op[0]);
       read_op(1, op[1]);
-      fill_k(t + 2, t & 1);
+      fill_k_full(t + 2, t & 1);
       s_next[0] = v16f{0};
       s_next[1] = v16f{0};
       float mx = -INFINITY;
@@ -527,7 +574,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
       keep_here(ks_next);
       keep_here(vs_next);
       __syncthreads();
-      fill_v(t + 1, (t + 1) & 1);
+      fill_v_full(t + 1, (t + 1) & 1);
     };
 
     int t = 0;
@@ -565,8 +612,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
       }
       // K_{t+2} replaces K_t and V_{t+1} replaces V_{t-1}: both last read in the
       // previous iteration
-      if (STEADY || t + 2 < n) fill_k(t + 2, t & 1);
-      if (has_next) fill_v(t + 1, (t + 1) & 1);
+      if constexpr (STEADY) {
+        fill_k_full(t + 2, t & 1);
+        fill_v_full(t + 1, (t + 1) & 1);
+      } else {
+        if (t + 2 < n) fill_k(t + 2, t & 1);
+        if (has_next) fill_v(t + 1, (t + 1) & 1);
+      }
       if (has_next) qk((t + 1) & 1, s_next);
 
       // p = 2^(s*c - m_ref), rounded to bf16 for P V; float32 row sum

@@ -93,6 +93,47 @@ __device__ __forceinline__ void keep_here(const T& x) {
 // (speculating its body into unconditional vector work).
 __device__ __forceinline__ void rare_branch() { asm volatile(""); }
 
+// ---- direct global -> LDS copies (16 bytes per lane) ----
+// Lane l's 16 bytes land at LDS byte address lds + 16 l (lds is wave-uniform; the
+// instruction takes it from M0). The copies are issued as inline assembly on purpose:
+// the compiler then does not track them, and in particular does not make every later
+// LDS read wait for all copies in flight (it cannot tell which buffer a copy writes).
+// Completion is the caller's job: s_waitcnt vmcnt(0) in each wave, then a workgroup
+// barrier, before any wave reads the buffer; and no copy may target a buffer that a wave
+// can still be reading. M0 is written here; the compiler sets M0 right before each of
+// its own uses, and this code has no other M0 user.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void*)p;
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// source = base (wave-uniform) + off (per lane, bytes)
+__device__ __forceinline__ void lds_copy16(const void* base, uint32_t off, uint32_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint64_t bu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(bu),
+               "s"(__builtin_amdgcn_readfirstlane((int)lds))
+               : "memory", "m0");
+#endif
+}
+// source = src (per lane)
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
+               "s"(__builtin_amdgcn_readfirstlane((int)lds))
+               : "memory", "m0");
+#endif
+}
+#pragma clang diagnostic pop
+// Wait for this wave's outstanding vector memory operations (the copies above included).
+__device__ __forceinline__ void wait_vmem() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#endif
+}
+
 // max of a value across lanes i and i+32.
 __device__ __forceinline__ float max_across_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
