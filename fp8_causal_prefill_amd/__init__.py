@@ -94,9 +94,11 @@ def _outputs(q, B, Hq, S, Dv, o, lse, return_lse):
 
 
 def attn_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, scale_block: int, softmax_scale=None, o=None, lse=None,
-                 return_lse: bool = False):
+                 return_lse: bool = False, lean: bool = False):
     """Causal attention on e4m3 codes (uint8 tensors [B, H, S, D]) with float32 block
-    scales [B, H, ceil(S / scale_block)]. Returns (o bfloat16 [B, Hq, S, Dv], lse or None)."""
+    scales [B, H, ceil(S / scale_block)]. Returns (o bfloat16 [B, Hq, S, Dv], lse or None).
+    lean=True calls zyfa_attn_fwd_fp8_lean (linear probability codes, the faster opt-in
+    mode) instead of zyfa_attn_fwd_fp8."""
     pq = _dev(q, "q", torch.uint8, 4)
     pk = _dev(k, "k", torch.uint8, 4)
     pv = _dev(v, "v", torch.uint8, 4)
@@ -110,9 +112,10 @@ def attn_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, scale_block: int, softmax_s
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(Dqk)
     o, po, lse, plse = _outputs(q, B, Hq, S, Dv, o, lse, return_lse)
-    st = load().zyfa_attn_fwd_fp8(pq, pk, pv, psq, psk, psv, scale_block, po, plse, B, Hq, Hkv, S, Dqk, Dv,
-                                  float(softmax_scale), _stream())
-    _lib.check(st, "zyfa_attn_fwd_fp8")
+    name = "zyfa_attn_fwd_fp8_lean" if lean else "zyfa_attn_fwd_fp8"
+    st = getattr(load(), name)(pq, pk, pv, psq, psk, psv, scale_block, po, plse, B, Hq, Hkv, S, Dqk, Dv,
+                               float(softmax_scale), _stream())
+    _lib.check(st, name)
     return o, lse
 
 

@@ -23,6 +23,7 @@ _SIGNATURES = {
     "zyfa_last_error": ([], ctypes.c_char_p),
     "zyfa_quantize_fp8": ([_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp], _i),
     "zyfa_attn_fwd_fp8": ([_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp], _i),
+    "zyfa_attn_fwd_fp8_lean": ([_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp], _i),
     "zyfa_attn_fwd_bf16": ([_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp], _i),
 }
 

@@ -55,6 +55,10 @@
 namespace zyfa {
 
 constexpr float kLazyThreshold = 8.0f;
+// Lean probabilities: code = round(8 y + kLeanBias) for p = 2^y. 56 is the code of 1.0;
+// the linear code overestimates 2^y inside each binade by 0 to 0.69 codes (mean 0.46),
+// and subtracting that mean minimises the error of the normalised output.
+constexpr float kLeanBias = 56.0f - 0.46f;
 
 template <bool FP8, int DQK>
 struct Cfg {
@@ -108,8 +112,9 @@ using QOp = typename std::conditional<FP8, v8i, v8bf>::type;
 // 16-key run) occupy 8 consecutive rows.
 __device__ __forceinline__ int fp8_vrow(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
-template <bool FP8, int DQK>
+template <bool FP8, int DQK, bool LEAN>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
+  static_assert(FP8 || !LEAN, "lean probabilities are an FP8 mode");
   using C = Cfg<FP8, DQK>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   char* const kring = smem;                // [2 buffers][column blocks][BN rows][64 bytes]
@@ -385,6 +390,30 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
     float rv_prev = 1.0f;
     int la = 0;
 
+    // e4m3 codes of four probabilities p = 2^(s c - bias) of one query row (s: raw
+    // scores j0..j0+3 of a 32-key group), packed low byte first. Exact mode: hardware
+    // exponential, then round-to-nearest-even conversion. Lean mode ("Lean P: Linear
+    // Approximation of the FP8 Code"): the code of 2^y is close to 8 y + 56 (eight codes
+    // per binade, 56 = 1.0), so it is taken as round-half-even(8 y + kLeanBias) clamped to
+    // [0, 255] (y < 1 keeps it below 64): one FMA and one conversion per value instead of
+    // an exponential and half a conversion.
+    auto p_codes = [&](const v16f& sv, int j0, float c, float bias) -> int {
+      if constexpr (LEAN) {
+        const float c8 = 8.0f * c, b8 = fmaf(-8.0f, bias, kLeanBias);
+        unsigned r = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[j0 + 0], c8, b8), 0, 0u);
+        r = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[j0 + 1], c8, b8), 1, r);
+        r = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[j0 + 2], c8, b8), 2, r);
+        r = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[j0 + 3], c8, b8), 3, r);
+        return (int)r;
+      } else {
+        const float p0 = fast_exp2(fmaf(sv[j0 + 0], c, -bias));
+        const float p1 = fast_exp2(fmaf(sv[j0 + 1], c, -bias));
+        const float p2 = fast_exp2(fmaf(sv[j0 + 2], c, -bias));
+        const float p3 = fast_exp2(fmaf(sv[j0 + 3], c, -bias));
+        return cvt_pk_fp8<true>(p2, p3, cvt_pk_fp8<false>(p0, p1, 0));
+      }
+    };
+
     // bring O and the row sum to the units of the P about to be added: the reference
     // change (alpha, a power of two; the in-flight P gets it through its E8M0 scale) and
     // the V-scale mantissa ratio. Both are rare: the branch is uniform per wave.
@@ -443,11 +472,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
       for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const float p0 = fast_exp2(fmaf(s_cur[g][4 * w + 0], c_cur, -bias));
-          const float p1 = fast_exp2(fmaf(s_cur[g][4 * w + 1], c_cur, -bias));
-          const float p2 = fast_exp2(fmaf(s_cur[g][4 * w + 2], c_cur, -bias));
-          const float p3 = fast_exp2(fmaf(s_cur[g][4 * w + 3], c_cur, -bias));
-          pw[4 * g + w] = cvt_pk_fp8<true>(p2, p3, cvt_pk_fp8<false>(p0, p1, 0));
+          pw[4 * g + w] = p_codes(s_cur[g], 4 * w, c_cur, bias);
         }
       p_cur = v8i{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
       sp_prev = kE8M0One + eb_cur;
@@ -522,20 +547,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < NSLOT; ++i) {
-        if (i < NQK)
-          s_next[i & 1] = mfma_fp8(op[i % 3], qreg[i >> 1], s_next[i & 1]);
-        else if (i < NQK + 4)
-          oacc[i - NQK] = mfma_fp8_scaled(op[i % 3], p_prev, oacc[i - NQK], svr, sp);
-        else
-          rs_acc = mfma_fp8_scaled(ones_fp8, p_prev, rs_acc, k127, sp);
+        // operand reads first, then the vector share, then the matrix instruction: the
+        // wait for the operands of instruction i (read two slots earlier) comes after
+        // this slot's vector work has issued
         if (i + 2 < NSLOT) read_op(i + 2, op[(i + 2) % 3]);
         if (i < 8) {
           const int g = i >> 2, w = i & 3;
-          const float p0 = fast_exp2(fmaf(s_cur[g][4 * w + 0], c_cur, -bias));
-          const float p1 = fast_exp2(fmaf(s_cur[g][4 * w + 1], c_cur, -bias));
-          const float p2 = fast_exp2(fmaf(s_cur[g][4 * w + 2], c_cur, -bias));
-          const float p3 = fast_exp2(fmaf(s_cur[g][4 * w + 3], c_cur, -bias));
-          p_cur[i] = cvt_pk_fp8<true>(p2, p3, cvt_pk_fp8<false>(p0, p1, 0));
+          p_cur[i] = p_codes(s_cur[g], 4 * w, c_cur, bias);
           keep_here(p_cur[i]);
         }
         if (i >= NQK + 1 && i >= 6) {  // the scores of tile t+1 are complete: row maxima
@@ -546,6 +564,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
             for (int r = r0; r < r1; ++r) mx = fmaxf(fmaxf(mx, s_next[0][r]), s_next[1][r]);
           }
         }
+        if (i < NQK)
+          s_next[i & 1] = mfma_fp8(op[i % 3], qreg[i >> 1], s_next[i & 1]);
+        else if (i < NQK + 4)
+          oacc[i - NQK] = mfma_fp8_scaled(op[i % 3], p_prev, oacc[i - NQK], svr, sp);
+        else
+          rs_acc = mfma_fp8_scaled(ones_fp8, p_prev, rs_acc, k127, sp);
         __builtin_amdgcn_sched_barrier(0);
       }
       // the products of this iteration stay in its slots (the next iteration's unit fix
@@ -692,7 +716,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   }
 }
 
-template <bool FP8, int DQK>
+template <bool FP8, int DQK, bool LEAN = false>
 static hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   using C = Cfg<FP8, DQK>;
   AttnParams p;
@@ -713,11 +737,12 @@ static hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   p.n_qtiles = (a.S + C::BM - 1) / C::BM;
   p.scale_log2 = a.softmax_scale * kLog2e;
   const long long grid = (long long)p.n_qtiles * a.B * a.Hq;
-  hipLaunchKernelGGL((attn_fwd_kernel<FP8, DQK>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<FP8, DQK, LEAN>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_fwd_fp8(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_attn_fwd_fp8(const AttnArgs& a, bool lean, hipStream_t stream) {
+  if (lean) return a.Dqk == 192 ? launch<true, 192, true>(a, stream) : launch<true, 128, true>(a, stream);
   return a.Dqk == 192 ? launch<true, 192>(a, stream) : launch<true, 128>(a, stream);
 }
 

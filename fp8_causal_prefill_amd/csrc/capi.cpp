@@ -97,9 +97,10 @@ zyfa_status zyfa_quantize_fp8(const void* x, int x_is_bf16, uint8_t* codes, floa
   return ok();
 }
 
-zyfa_status zyfa_attn_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_scale,
-                              const float* k_scale, const float* v_scale, int scale_block, uint16_t* o, float* lse,
-                              int B, int Hq, int Hkv, int S, int Dqk, int Dv, float softmax_scale, void* stream) {
+static zyfa_status attn_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_scale,
+                            const float* k_scale, const float* v_scale, int scale_block, uint16_t* o, float* lse,
+                            int B, int Hq, int Hkv, int S, int Dqk, int Dv, float softmax_scale, void* stream,
+                            bool lean) {
   zyfa_status st = check_attn_common(q, k, v, o, lse, B, Hq, Hkv, S, Dqk, Dv, softmax_scale);
   if (st != ZYFA_OK) return st;
   if (!q_scale || !k_scale || !v_scale) return fail(ZYFA_ERR_INVALID_ARGUMENT, "scale pointers must be non-null");
@@ -109,9 +110,24 @@ zyfa_status zyfa_attn_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t*
     return fail(ZYFA_ERR_INVALID_ARGUMENT, "scale_block must be 64 or 128 (got %d)", scale_block);
 
   zyfa::AttnArgs a{q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, S, Dqk, Dv, scale_block, softmax_scale};
-  hipError_t e = zyfa::launch_attn_fwd_fp8(a, (hipStream_t)stream);
+  hipError_t e = zyfa::launch_attn_fwd_fp8(a, lean, (hipStream_t)stream);
   if (e != hipSuccess) return fail(ZYFA_ERR_LAUNCH, "attention launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+zyfa_status zyfa_attn_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_scale,
+                              const float* k_scale, const float* v_scale, int scale_block, uint16_t* o, float* lse,
+                              int B, int Hq, int Hkv, int S, int Dqk, int Dv, float softmax_scale, void* stream) {
+  return attn_fp8(q, k, v, q_scale, k_scale, v_scale, scale_block, o, lse, B, Hq, Hkv, S, Dqk, Dv, softmax_scale,
+                  stream, false);
+}
+
+zyfa_status zyfa_attn_fwd_fp8_lean(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_scale,
+                                   const float* k_scale, const float* v_scale, int scale_block, uint16_t* o,
+                                   float* lse, int B, int Hq, int Hkv, int S, int Dqk, int Dv, float softmax_scale,
+                                   void* stream) {
+  return attn_fp8(q, k, v, q_scale, k_scale, v_scale, scale_block, o, lse, B, Hq, Hkv, S, Dqk, Dv, softmax_scale,
+                  stream, true);
 }
 
 zyfa_status zyfa_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,

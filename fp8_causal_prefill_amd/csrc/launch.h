@@ -21,7 +21,8 @@ struct AttnArgs {
   float softmax_scale;
 };
 
-hipError_t launch_attn_fwd_fp8(const AttnArgs& a, hipStream_t stream);
+// lean: probabilities as linear e4m3 codes instead of rounded exponentials
+hipError_t launch_attn_fwd_fp8(const AttnArgs& a, bool lean, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream);
 
 struct QuantArgs {

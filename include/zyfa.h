@@ -130,6 +130,26 @@ zyfa_status zyfa_attn_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t*
                               void* stream);
 
 /*
+ * zyfa_attn_fwd_fp8_lean -- zyfa_attn_fwd_fp8 with linear probability codes.
+ *
+ * Source: ZYFA page, section "Lean P: Linear Approximation of the FP8 Code" (the
+ * e4m3 code of 2^y is nearly linear in y, about 8 y plus a constant), and "Numerical
+ * Accuracy" (its error is 1.22-1.36 times that of exactly rounded probabilities).
+ *
+ * Same arguments, layouts, scales, errors and output as zyfa_attn_fwd_fp8. Only the
+ * probabilities differ: with y = s*c - bias the base-2 exponent of a probability after
+ * its block scaling (y < 1), its code is round-half-even(8 y + 55.54) clamped to
+ * [0, 255] instead of the round-to-nearest-even e4m3 code of 2^y: one fused multiply-add
+ * and one conversion per score, no exponential. The normalisation still uses the sum of
+ * exactly these codes' values, so outputs remain weighted averages. An opt-in fast mode:
+ * expect about 1.25 times the relative error of zyfa_attn_fwd_fp8.
+ */
+zyfa_status zyfa_attn_fwd_fp8_lean(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_scale,
+                                   const float* k_scale, const float* v_scale, int scale_block, uint16_t* o,
+                                   float* lse, int B, int Hq, int Hkv, int S, int Dqk, int Dv, float softmax_scale,
+                                   void* stream);
+
+/*
  * zyfa_attn_fwd_bf16 -- causal attention on bfloat16 inputs.
  *
  * Source: ZYFA page, Introduction and section "Throughput on Gaussian Inputs"

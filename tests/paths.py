@@ -38,13 +38,13 @@ def gpu_quantize(x, block, hadamard=False):
     return codes, scales
 
 
-def gpu_fp8(q, k, v, block, hadamard=False, scale=None, return_lse=True):
-    """fp32 numpy inputs -> GPU quantizer -> GPU FP8 attention. Returns numpy
-    (o float64, lse float64, (qc, qs, kc, ks, vc, vs) numpy)."""
+def gpu_fp8(q, k, v, block, hadamard=False, scale=None, return_lse=True, lean=False):
+    """fp32 numpy inputs -> GPU quantizer -> GPU FP8 attention (exact or lean
+    probabilities). Returns numpy (o float64, lse float64, (qc, qs, kc, ks, vc, vs) numpy)."""
     qc, qs = gpu_quantize(q, block, hadamard)
     kc, ks = gpu_quantize(k, block, hadamard)
     vc, vs = gpu_quantize(v, block, False)
-    o, lse = zy.attn_fwd_fp8(qc, kc, vc, qs, ks, vs, block, scale, return_lse=return_lse)
+    o, lse = zy.attn_fwd_fp8(qc, kc, vc, qs, ks, vs, block, scale, return_lse=return_lse, lean=lean)
     torch.cuda.synchronize()
     parts = tuple(t.cpu().numpy() for t in (qc, qs, kc, ks, vc, vs))
     return bf16_from_f64(o), (lse.cpu().numpy().astype(np.float64) if lse is not None else None), parts

@@ -36,7 +36,7 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"zyfa_abi_version", "zyfa_status_string", "zyfa_last_error", "zyfa_quantize_fp8",
-                          "zyfa_attn_fwd_fp8", "zyfa_attn_fwd_bf16"}
+                          "zyfa_attn_fwd_fp8", "zyfa_attn_fwd_fp8_lean", "zyfa_attn_fwd_bf16"}
     raw = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -52,8 +52,9 @@ def test_version_and_status_strings(lib):
 
 
 def fp8(lib, q=P, k=P2, v=P3, qs=P4, ks=P5, vs=P6, blk=128, o=P7, lse=None, B=1, Hq=4, Hkv=2, S=256, Dqk=128,
-        Dv=128, scale=0.088):
-    return lib.zyfa_attn_fwd_fp8(q, k, v, qs, ks, vs, blk, o, lse, B, Hq, Hkv, S, Dqk, Dv, scale, None)
+        Dv=128, scale=0.088, lean=False):
+    fn = lib.zyfa_attn_fwd_fp8_lean if lean else lib.zyfa_attn_fwd_fp8
+    return fn(q, k, v, qs, ks, vs, blk, o, lse, B, Hq, Hkv, S, Dqk, Dv, scale, None)
 
 
 def bf16(lib, q=P, k=P2, v=P3, o=P7, lse=None, B=1, Hq=4, Hkv=2, S=256, Dqk=128, Dv=128, scale=0.088):
@@ -78,12 +79,14 @@ def test_attention_argument_checks(lib, kw, expect):
     assert bf16(lib, **kw) == expect
     assert lib.zyfa_last_error() != b""
     assert fp8(lib, **kw) == expect
+    assert fp8(lib, lean=True, **kw) == expect
 
 
 @pytest.mark.parametrize("kw", [dict(qs=None), dict(ks=None), dict(vs=None), dict(vs=MIS), dict(blk=32),
                                 dict(blk=0), dict(blk=256)])
 def test_fp8_scale_checks(lib, kw):
     assert fp8(lib, **kw) == INVALID
+    assert fp8(lib, lean=True, **kw) == INVALID
 
 
 def quant(lib, x=P, bf=0, codes=P2, scales=P3, B=1, H=2, S=100, D=128, blk=64, had=0):

@@ -211,3 +211,45 @@ def test_bf16_short_and_ragged_lengths(S):
         print(f"bf16 S={S} Dqk={Dqk} rel-L2 {err:.3e}")
         assert err <= BF16_BAR
         assert np.max(np.abs(lse - rlse)) < 1e-3
+
+
+# ---- lean probabilities (zyfa_attn_fwd_fp8_lean) ----
+# The linear code adds a bounded, input-independent distortion to every probability, so
+# its error is a fixed multiple of the exact kernel's: the ZYFA page reports 1.22-1.36x;
+# the bar here is 1.5x the exact kernel's error on the same inputs (plus 1e-3 for tiny
+# cases where both are small), and never above 4e-2.
+LEAN_FACTOR = 1.5
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_fp8_lean_parity(shape):
+    B, Hq, Hkv, S, Dqk, Dv, block = shape
+    _case(shape, lean=True)
+    q, k, v = generate(custom(B, Hq, Hkv, S, Dqk, Dv, wid=600), seed=S)
+    scale = 1 / math.sqrt(Dqk)
+    o_lean, lse_lean, parts = gpu_fp8(q, k, v, block, scale=scale, lean=True)
+    o_exact, _, _ = gpu_fp8(q, k, v, block, scale=scale)
+    ro, rlse = oracle_attention_from_codes(parts, block, scale)
+    e_lean, e_exact = rel_l2(o_lean, ro), rel_l2(o_exact, ro)
+    print(f"fp8 lean rel-L2 {e_lean:.3e} (exact {e_exact:.3e})")
+    assert np.all(np.isfinite(o_lean))
+    assert e_lean <= LEAN_FACTOR * e_exact + 1e-3
+    assert e_lean <= 4e-2
+    # each weight is off by at most ~1 code (a factor 2^(1/8)); the log-sum-exp moves by less
+    assert np.max(np.abs(lse_lean - rlse)) < 0.1
+
+
+def test_fp8_lean_exact_special_cases():
+    # V == 1: still exactly 1 (the normalisation uses the same codes); Q == 0: every score
+    # equal, y = 0, code round(55.54) = 56 = 1.0 exactly, so O is the prefix mean of V
+    qc, kc, vc, qs, ks, vs = _quantized(1, 4, 2, 600, 128, 64, seed=1)
+    ones = torch.full_like(vc, 0x38)
+    o, _ = zy.attn_fwd_fp8(qc, kc, ones, qs, ks, torch.ones_like(vs), 64, lean=True)
+    assert torch.all(o.float() == 1.0)
+    qc, kc, vc, qs, ks, vs = _quantized(1, 2, 2, 500, 128, 128, seed=2)
+    vs = torch.exp2(torch.round(torch.log2(vs)))
+    o, _ = zy.attn_fwd_fp8(torch.zeros_like(qc), kc, vc, qs, ks, vs, 128, lean=True)
+    torch.cuda.synchronize()
+    vd = dequantize_blocks(vc.cpu().numpy(), vs.cpu().numpy(), 128)
+    ref = np.cumsum(vd, axis=2) / np.arange(1, 501)[None, None, :, None]
+    assert rel_l2(bf16_from_f64(o), ref) < 4e-3
