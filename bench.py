@@ -11,9 +11,10 @@ inputs. FLOPs follow the FlashAttention causal convention, 2 (Dqk + Dv) S^2 / 2 
 
 Prints one JSON line. ``value`` is FP8 whole-step throughput; the attention kernel
 alone is timed with HIP events on the stream it runs on and reported against the
-datasheet dense FP8 peak in ``roofline``; BF16 is reported in ``bf16``. The CPU
-baseline times the fp64 oracle on a bounded sample (one head, a block of query
-rows) on the host cores.
+datasheet dense FP8 peak in ``roofline``; the opt-in lean-probability FP8 mode is
+reported in ``fp8_lean`` and BF16 in ``bf16``. The CPU baseline times the fp64 oracle
+on a bounded sample (whole query heads, about 15 s) on the host cores; the heads it
+computed also give a full-size parity figure (``sampled_rel_l2_fp8``).
 """
 
 import argparse
@@ -109,6 +110,7 @@ def main():
     ap.add_argument("--workload", default="gqa32k")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-lean", action="store_true", help="skip the lean-probability FP8 mode")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -150,6 +152,7 @@ def main():
     ks = torch.empty((w.B, w.Hkv, nb), dtype=torch.float32, device=dev)
     vs = torch.empty((w.B, w.Hkv, nb), dtype=torch.float32, device=dev)
     o8 = torch.empty((w.B, w.Hq, w.S, w.Dv), dtype=torch.bfloat16, device=dev)
+    o8l = torch.empty_like(o8)
 
     stream = torch.cuda.current_stream()
     ev = []
@@ -181,6 +184,29 @@ def main():
     attn_med_s = float(np.median(attn_ms)) / 1e3
     print(f"[bench] fp8 step {step_s * 1e3:.3f} ms, attention kernel mean {attn_s * 1e3:.3f} ms "
           f"(median {attn_med_s * 1e3:.3f})", file=sys.stderr, flush=True)
+
+    # ---------------- FP8 attention, lean probabilities (opt-in mode) ----------------
+    lean = None
+    if not args.no_lean:
+        evl = []
+        for _ in range(max(args.warmup // 2, 1)):
+            zy.attn_fwd_fp8(qc, kc, vc, qs, ks, vs, blk, scale, o=o8l, lean=True)
+        torch.cuda.synchronize()
+        lsteps = max(args.steps // 2, 1)
+        for _ in range(lsteps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            zy.attn_fwd_fp8(qc, kc, vc, qs, ks, vs, blk, scale, o=o8l, lean=True)
+            e1.record(stream)
+            evl.append((e0, e1))
+        torch.cuda.synchronize()
+        lms = [a.elapsed_time(b) for a, b in evl]
+        l_s = float(np.mean(lms)) / 1e3
+        print(f"[bench] fp8 lean attention kernel mean {l_s * 1e3:.3f} ms", file=sys.stderr, flush=True)
+        lean = {"entry_point": "zyfa_attn_fwd_fp8_lean", "tflops": flops / l_s / 1e12, "ms": l_s * 1e3,
+                "ms_median": float(np.median(lms)), "frac_of_fp8_peak": flops / l_s / 1e12 / PEAK_FP8,
+                "steps": lsteps}
 
     # ---------------- BF16 attention ----------------
     bf16 = None
@@ -236,6 +262,7 @@ def main():
                      "frac": achieved / PEAK_FP8, "traffic": hbm_traffic(w.name, "fp8"),
                      "kernel": "attn_fwd_kernel<FP8, 128>", "kernel_ms_mean": attn_s * 1e3,
                      "kernel_ms_median": attn_med_s * 1e3},
+        "fp8_lean": lean,
         "bf16": bf16,
     }
 
@@ -249,6 +276,12 @@ def main():
             den += float(np.sum(ref ** 2))
         line["cpu_baseline"] = cpu
         line["sampled_rel_l2_fp8"] = math.sqrt(num / den)
+        if lean is not None:
+            num = 0.0
+            for hq, ref in refs.items():
+                got = o8l[0, hq].float().cpu().numpy().astype(np.float64)
+                num += float(np.sum((got - ref) ** 2))
+            lean["sampled_rel_l2"] = math.sqrt(num / den)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

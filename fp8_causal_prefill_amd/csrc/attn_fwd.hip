@@ -15,11 +15,13 @@
 //    back out; each row is normalised by the sum of exactly the rounded values
 //    that multiply V, computed by one more matrix instruction.
 //  * "Lean P": probabilities are formed in base 2, p = 2^x with x the score minus
-//    the row maximum in base-2 units (this kernel evaluates 2^x with the hardware
-//    exponential and rounds it to e4m3 - the page's "exact P").
+//    the row maximum in base-2 units. The default mode evaluates 2^x with the hardware
+//    exponential and rounds it to e4m3 (the page's "exact P"); the lean mode takes the
+//    e4m3 code as a linear function of x (the page's lean P).
 //
-// Work decomposition (one workgroup = 4 waves = 128 query rows of one head, two
-// workgroups per CU):
+// Work decomposition (one workgroup = 32 query rows per wave of one head: 8 waves,
+// one workgroup per CU, for FP8 at D = 128; 4 waves, two workgroups per CU otherwise;
+// always two waves per SIMD):
 //  * Each wave owns 32 query rows and computes S^T = K Q^T on 32x32 MFMA tiles,
 //    so every lane holds the scores of one query row (lane % 32) for half of the
 //    keys of a tile; row maxima need one lane-half exchange (v_permlane32_swap).
@@ -63,7 +65,9 @@ constexpr float kLeanBias = 56.0f - 0.46f;
 template <bool FP8, int DQK>
 struct Cfg {
   static constexpr int DV = 128;
-  static constexpr int WAVES = 4;
+  // FP8 at D = 128: eight waves (256 query rows share each K/V tile copy, halving the
+  // copy traffic that competes with the operand reads for LDS); otherwise four
+  static constexpr int WAVES = (FP8 && DQK == 128) ? 8 : 4;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;  // query rows per workgroup
   static constexpr int BN = 64;          // keys per tile
@@ -88,7 +92,7 @@ struct Cfg {
   static constexpr int NKS = DQK / KSTEP;
   static_assert(BN * KROW % (16 * THREADS) == 0 && BN * VROW % (16 * THREADS) == 0, "tile load split");
   static_assert(DQK % KSTEP == 0, "head dim must divide the MFMA depth");
-  static_assert(BM == 2 * BN, "steady iterations rely on two key tiles per query tile");
+  static_assert(BM % (2 * BN) == 0, "steady iterations rely on an even number of key tiles per query tile");
 };
 
 struct AttnParams {
@@ -113,7 +117,7 @@ using QOp = typename std::conditional<FP8, v8i, v8bf>::type;
 __device__ __forceinline__ int fp8_vrow(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 template <bool FP8, int DQK, bool LEAN>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(AttnParams p) {
   static_assert(FP8 || !LEAN, "lean probabilities are an FP8 mode");
   using C = Cfg<FP8, DQK>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
@@ -325,8 +329,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
 
   // iterations t < n_steady need no causal mask on tile t+1 in any wave and prefetch
   // K_{t+2}: their bodies are branch-free and carry a fixed instruction schedule. With
-  // BM = 2 BN and n_steady even, every tile they fetch (t + 2 <= (q0_wg + 1) / BN - 1)
-  // ends before row q0_wg < S: no clamping.
+  // BM a multiple of 2 BN, (q0_wg + 1) / BN - 1 is odd, so the even n_steady is at most
+  // q0_wg / BN - 2 and every tile they fetch (t + 2 <= q0_wg / BN - 1) ends before row
+  // q0_wg < S: no clamping.
   const int n_steady = max(0, min(n - 2, (q0_wg + 1) / C::BN - 1)) & ~1;
 
   v16f sa[2], sb[2];
