@@ -85,7 +85,9 @@ struct Cfg {
   static constexpr int KBLK = BN * 64;  // bytes of one column block
   static constexpr int KBUF = BN * KROW;
   static constexpr int VBUF = BN * VROW;
-  static constexpr int LDS_BYTES = 2 * KBUF + 2 * VBUF;
+  // LDS ring depth per tensor: two buffers, one barrier per iteration
+  static constexpr int NBUF = 2;
+  static constexpr int LDS_BYTES = NBUF * (KBUF + VBUF);
   static constexpr int KCHUNKS = BN * KROW / 16 / THREADS;  // 16-byte loads per thread per tile
   static constexpr int VCHUNKS = BN * VROW / 16 / THREADS;
   static constexpr int KSTEP = FP8 ? 64 : 16;  // MFMA reduction depth
@@ -122,7 +124,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   using C = Cfg<FP8, DQK>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   char* const kring = smem;                // [2 buffers][column blocks][BN rows][64 bytes]
-  char* const vring = smem + 2 * C::KBUF;  // same layout for V
+  char* const vring = smem + C::NBUF * C::KBUF;  // same layout for V
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -319,10 +321,11 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   fill_v(0, 0);
   if (n > 1) fill_k(1, 1);
   if constexpr (FP8) {
-    // the PV stage of the first iteration multiplies an all-zero P with V buffer 1:
-    // make that buffer finite
+    // the PV stage of the first iteration multiplies an all-zero P with the buffer of
+    // "V_-1": make that buffer finite
 #pragma unroll
-    for (int i = 0; i < C::VCHUNKS; ++i) *(v4i*)(vring + C::VBUF + (tid + i * C::THREADS) * 16) = v4i{0, 0, 0, 0};
+    for (int i = 0; i < C::VCHUNKS; ++i)
+      *(v4i*)(vring + (C::NBUF - 1) * C::VBUF + (tid + i * C::THREADS) * 16) = v4i{0, 0, 0, 0};
   }
   wait_fills();
   __syncthreads();
@@ -336,6 +339,8 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
 
   v16f sa[2], sb[2];
   qk(0, sa);
+  // every wave has read K_0 before any wave's first iteration copies a tile into its buffer
+  __syncthreads();
   mask(sa, 0);
   float c_cur = c_q;
   if constexpr (FP8) c_cur *= kscale[0];
@@ -466,9 +471,9 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       fix_units();
       const float ks_pf = kscale[sidx(t + 2)];
       const float vs_pf = vscale[sidx(t + 2)];
-      if (STEADY || t + 2 < n) fill_k(t + 2, t & 1);
-      if (has_next) qk((t + 1) & 1, s_next);
-      pv(p_prev, sp_prev, sv_prev, (t + 1) & 1);
+      if (STEADY || t + 2 < n) fill_k(t + 2, (t + 2) % C::NBUF);
+      if (has_next) qk((t + 1) % C::NBUF, s_next);
+      pv(p_prev, sp_prev, sv_prev, (t + C::NBUF - 1) % C::NBUF);
 
       // p = 2^(s*c - m_ref - eb): the block maximum lands in [1, 2), rounded to e4m3
       const float bias = m_ref + (float)eb_cur;
@@ -506,7 +511,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       ks_next = ks_pf;
       vs_next = vs_pf;
       __syncthreads();
-      if (has_next) fill_v(t + 1, (t + 1) & 1);
+      if (has_next) fill_v(t + 1, (t + 1) % C::NBUF);
     };
 
     // Steady iteration, hand-ordered: slot i issues matrix instruction i (QK of tile t+1,
@@ -518,8 +523,8 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       constexpr int NQK = 2 * C::NKS;
       constexpr int NSLOT = NQK + 5;
       fix_units();
-      const char* kb = kring + ((t + 1) & 1) * C::KBUF;
-      const char* vb = vring + ((t + 1) & 1) * C::VBUF;  // V of tile t-1
+      const char* kb = kring + ((t + 1) % C::NBUF) * C::KBUF;
+      const char* vb = vring + ((t + C::NBUF - 1) % C::NBUF) * C::VBUF;  // V of tile t-1
       const float bias = m_ref + (float)eb_cur;
       const int svr = opaque(sv_prev);
       const int sp = sp_prev;
@@ -545,10 +550,15 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       const float vs_pf = vscale[sidx(t + 2)];
       read_op(0, op[0]);
       read_op(1, op[1]);
-      fill_k_full(t + 2, t & 1);
+      fill_k_full(t + 2, (t + 2) % C::NBUF);
       s_next[0] = v16f{0};
       s_next[1] = v16f{0};
-      float mx = -INFINITY;
+      // tile t's values, before the update for tile t+1 inside the slots replaces them
+      const float c_t = c_cur;
+      const int eb_t = eb_cur, sv_t = sv_cur;
+      const float rv_t = rv_cur;
+      float mx = -INFINITY, xmax = 0.0f, c_next = 0.0f;
+      bool grow = false;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < NSLOT; ++i) {
@@ -558,16 +568,33 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
         if (i + 2 < NSLOT) read_op(i + 2, op[(i + 2) % 3]);
         if (i < 8) {
           const int g = i >> 2, w = i & 3;
-          p_cur[i] = p_codes(s_cur[g], 4 * w, c_cur, bias);
+          p_cur[i] = p_codes(s_cur[g], 4 * w, c_t, bias);
           keep_here(p_cur[i]);
         }
-        if (i >= NQK + 1 && i >= 6) {  // the scores of tile t+1 are complete: row maxima
-          const int r0 = i == NSLOT - 3 ? 0 : (i == NSLOT - 2 ? 6 : 11);
-          const int r1 = i == NSLOT - 3 ? 6 : (i == NSLOT - 2 ? 11 : 16);
-          if (i >= NSLOT - 3) {
+        // the scores of tile t+1 are complete one slot after the last QK instruction:
+        // row maxima in slots NSLOT-4 and NSLOT-3, then the lazy reference update for
+        // tile t+1 in the last two slots, beside the PV and row-sum instructions
+        if (i == NSLOT - 4 || i == NSLOT - 3) {
+          const int r0 = i == NSLOT - 4 ? 0 : 8;
 #pragma unroll
-            for (int r = r0; r < r1; ++r) mx = fmaxf(fmaxf(mx, s_next[0][r]), s_next[1][r]);
-          }
+          for (int r = r0; r < r0 + 8; ++r) mx = fmaxf(fmaxf(mx, s_next[0][r]), s_next[1][r]);
+        }
+        if (i == NSLOT - 2) {
+          // (the scales were loaded an iteration earlier; opaque keeps their use, and the
+          // wait for their loads, in this slot)
+          c_next = c_q * opaque_f(ks_next);
+          xmax = max_across_halves(mx) * c_next;
+          grow = xmax > m_ref + kLazyThreshold;
+          rescale = __any(grow);
+        }
+        if (i == NSLOT - 1) {
+          const float m_new = grow ? ceilf(xmax) : m_ref;
+          la = (int)(m_ref - m_new);
+          alpha = fast_exp2((float)la);
+          m_ref = m_new;
+          vsplit(opaque_f(vs_next), rv_cur, sv_cur);
+          eb_cur = block_exp(xmax);
+          c_cur = c_next;
         }
         if (i < NQK)
           s_next[i & 1] = mfma_fp8(op[i % 3], qreg[i >> 1], s_next[i & 1]);
@@ -582,28 +609,15 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
 #pragma unroll
       for (int d = 0; d < 4; ++d) keep_here(oacc[d]);
       keep_here(rs_acc);
-      sp_prev = kE8M0One + eb_cur;
-      sv_prev = sv_cur;
-      rv_prev = rv_cur;
-
-      const float c_next = c_q * ks_next;
-      const float xmax = max_across_halves(mx) * c_next;
-      const bool grow = xmax > m_ref + kLazyThreshold;
-      rescale = __any(grow);
-      const float m_new = grow ? ceilf(xmax) : m_ref;
-      la = (int)(m_ref - m_new);
-      alpha = fast_exp2((float)la);
-      m_ref = m_new;
-      vsplit(vs_next, rv_cur, sv_cur);
-      eb_cur = block_exp(xmax);
-      c_cur = c_next;
-      wait_fills();
+      sp_prev = kE8M0One + eb_t;
+      sv_prev = sv_t;
+      rv_prev = rv_t;
       ks_next = ks_pf;
       vs_next = vs_pf;
-      keep_here(ks_next);
-      keep_here(vs_next);
+      wait_fills();
       __syncthreads();
-      fill_v_full(t + 1, (t + 1) & 1);
+      // V_{t+1} replaces V_{t-1}, last read by this iteration's PV products
+      fill_v_full(t + 1, (t + 1) % C::NBUF);
     };
 
     int t = 0;
@@ -617,7 +631,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     }
     // drain: PV of the last tile (its P is pb if n - 1 is even, else pa)
     fix_units();
-    pv(((n - 1) & 1) ? pa : pb, sp_prev, sv_prev, (n - 1) & 1);
+    pv(((n - 1) & 1) ? pa : pb, sp_prev, sv_prev, (n - 1) % C::NBUF);
 #pragma unroll
     for (int d = 0; d < 4; ++d) pin_acc(oacc[d]);
     pin_acc(rs_acc);

@@ -66,6 +66,15 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
+// The same for a float: the value is only available from this point of the program on,
+// so work depending on it cannot be hoisted above (e.g. out of a pipeline slot).
+__device__ __forceinline__ float opaque_f(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(x));
+#endif
+  return x;
+}
+
 // Materialise a matrix accumulator here, in the current (uniform) control flow. A
 // matrix instruction reads its operands from all 64 lanes whatever EXEC holds, so it
 // must not be moved into a lane-divergent region (such as a guarded output store),
