@@ -102,6 +102,64 @@ def cpu_baseline(w, q, k, v, target_s=15.0):
             "seconds": round(secs, 3)}, refs
 
 
+def time_kernel(fn, steps, warmup, stream, torch):
+    """Mean and median milliseconds of fn() from HIP events on the stream it launches on."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    return float(np.mean(ms)), float(np.median(ms))
+
+
+def other_workloads(names, steps, warmup, torch, zy):
+    """Kernel throughput on the other benchmark shapes (4K MHA, 32K MLA, 16K activation-like
+    with and without the Hadamard rotation of Q and K): FP8 exact and lean, and BF16.
+    Reported from the median launch time (these shorter runs see occasional outliers)."""
+    from workloads import WORKLOADS, generate
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name in names:
+        w = WORKLOADS[name]
+        q, k, v = generate(w, seed=0)
+        dev = torch.device("cuda:0")
+        qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+        del q, k, v
+        rec = {"shape": f"B={w.B} Hq={w.Hq} Hkv={w.Hkv} S={w.S} Dqk={w.Dqk} Dv={w.Dv}", "flops": w.flops}
+        for had in ((False, True) if w.dist == "activation" else (False,)):
+            qc, qs = zy.quantize_fp8(qd, w.scale_block, had)
+            kc, ks = zy.quantize_fp8(kd, w.scale_block, had)
+            vc, vs = zy.quantize_fp8(vd, w.scale_block, False)
+            o = torch.empty((w.B, w.Hq, w.S, w.Dv), dtype=torch.bfloat16, device=dev)
+            tag = "_hadamard" if had else ""
+            for mode in ("fp8", "fp8_lean"):
+                lean = mode == "fp8_lean"
+                ms, med = time_kernel(lambda: zy.attn_fwd_fp8(qc, kc, vc, qs, ks, vs, w.scale_block, w.softmax_scale,
+                                                              o=o, lean=lean), steps, warmup, stream, torch)
+                rec[mode + tag] = {"ms_mean": ms, "ms": med, "tflops": w.flops / med / 1e9,
+                                   "frac_of_fp8_peak": w.flops / med / 1e9 / PEAK_FP8}
+            del qc, kc, vc
+        qb, kb, vb = qd.to(torch.bfloat16), kd.to(torch.bfloat16), vd.to(torch.bfloat16)
+        ob = torch.empty((w.B, w.Hq, w.S, w.Dv), dtype=torch.bfloat16, device=dev)
+        ms, med = time_kernel(lambda: zy.attn_fwd_bf16(qb, kb, vb, w.softmax_scale, o=ob), steps, warmup, stream, torch)
+        rec["bf16"] = {"ms_mean": ms, "ms": med, "tflops": w.flops / med / 1e9,
+                       "frac_of_bf16_peak": w.flops / med / 1e9 / PEAK_BF16}
+        out[name] = rec
+        print(f"[bench] {name}: fp8 {rec['fp8']['ms']:.3f} ms, lean {rec['fp8_lean']['ms']:.3f} ms, "
+              f"bf16 {rec['bf16']['ms']:.3f} ms", file=sys.stderr, flush=True)
+        del qd, kd, vd, qb, kb, vb, o, ob
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +169,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-lean", action="store_true", help="skip the lean-probability FP8 mode")
+    ap.add_argument("--no-others", action="store_true", help="skip the other workload shapes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -265,6 +324,10 @@ def main():
         "fp8_lean": lean,
         "bf16": bf16,
     }
+
+    if not args.no_others:
+        others = [n for n in ("mha4k", "mla32k", "act16k") if n != w.name]
+        line["other_workloads"] = other_workloads(others, max(args.steps // 5, 5), max(args.warmup // 10, 5), torch, zy)
 
     if not args.no_cpu:
         cpu, refs = cpu_baseline(w, q, k, v)
