@@ -378,10 +378,12 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     v16f rs_acc = v16f{0};  // rounded row sum, accumulated on the MFMA (any register holds it)
     float rv_o = 1.0f;      // O holds sum(w v) / rv_o
 
+    // (the scale is the same in every lane: integer fields of its bits, on the scalar
+    // unit; for a normal float, sv is its biased exponent and rv keeps sign and mantissa)
     auto vsplit = [&](float vsc, float& rv, int& sv) {
-      int ev;
-      rv = 2.0f * frexpf(vsc, &ev);
-      sv = kE8M0One + ev - 1;
+      const int b = __builtin_amdgcn_readfirstlane(__float_as_int(vsc));
+      sv = (b >> 23) & 0xff;
+      rv = __int_as_float((b & (int)0x807fffff) | 0x3f800000);
     };
     // K and V scales of tile t+1 while iteration t runs; the loads for tile t+2 are
     // issued at the top of iteration t, ahead of the tile fills whose wait covers them
@@ -398,7 +400,13 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     v8i pa = v8i{0}, pb = v8i{0};
     int sp_prev = kE8M0One, sv_prev = kE8M0One;
     float rv_prev = 1.0f;
-    int la = 0;
+    // Lazy reference: m_ref moves (to the ceiling of a row's new maximum) only for rows
+    // whose maximum exceeds it by more than kLazyThreshold. The iteration that sees tile
+    // t+1's maxima takes the decision (grow; rescale = some row grows) and the block
+    // exponent against the current m_ref; fix_units at the top of the next iteration
+    // moves m_ref, recomputes that exponent and rescales O (rare, wave-uniform branch).
+    float xmax_pend = 0.0f;  // tile t+1's row maxima in base-2 units
+    bool grow = false;
 
     // e4m3 codes of four probabilities p = 2^(s c - bias) of one query row (s: raw
     // scores j0..j0+3 of a 32-key group), packed low byte first. Exact mode: hardware
@@ -424,17 +432,27 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       }
     };
 
-    // bring O and the row sum to the units of the P about to be added: the reference
-    // change (alpha, a power of two; the in-flight P gets it through its E8M0 scale) and
-    // the V-scale mantissa ratio. Both are rare: the branch is uniform per wave.
+    // bring O and the row sum to the units of the P about to be added: the pending
+    // reference move (a power of two, 2^(m_ref - m_new); the in-flight P gets it through
+    // its E8M0 scale) and the V-scale mantissa ratio. Both are rare: the branch is
+    // uniform per wave.
     auto fix_units = [&]() {
-      if (rescale || rv_prev != rv_o) {
+      if (rescale || __float_as_int(rv_prev) != __float_as_int(rv_o)) {
         rare_branch();
-        const float f = (rescale ? alpha : 1.0f) * (rv_o / rv_prev);
+        int la = 0;
+        float a = 1.0f;
+        if (rescale) {
+          const float m_new = grow ? ceilf(xmax_pend) : m_ref;
+          la = (int)(m_ref - m_new);
+          a = fast_exp2((float)la);
+          m_ref = m_new;
+          eb_cur = block_exp(xmax_pend);
+        }
+        const float f = a * (rv_o / rv_prev);
 #pragma unroll
         for (int d = 0; d < 4; ++d) oacc[d] *= f;
         if (rescale) {
-          rs_acc[0] *= alpha;
+          rs_acc[0] *= a;
           sp_prev = max(sp_prev + la, 0);
         }
         rv_o = rv_prev;
@@ -496,13 +514,10 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
         xmax = rowmax(s_next) * c_next;
       }
       if (has_next) {
-        // lazy reference update, branch-free: rows that do not grow keep m_ref (alpha = 1)
-        const bool grow = xmax > m_ref + kLazyThreshold;
+        // lazy reference decision (carried out by the next fix_units)
+        grow = xmax > m_ref + kLazyThreshold;
         rescale = __any(grow);
-        const float m_new = grow ? ceilf(xmax) : m_ref;
-        la = (int)(m_ref - m_new);
-        alpha = fast_exp2((float)la);
-        m_ref = m_new;
+        xmax_pend = xmax;
         vsplit(vs_next, rv_cur, sv_cur);
         eb_cur = block_exp(xmax);
         c_cur = c_next;
@@ -558,7 +573,6 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       const int eb_t = eb_cur, sv_t = sv_cur;
       const float rv_t = rv_cur;
       float mx = -INFINITY, xmax = 0.0f, c_next = 0.0f;
-      bool grow = false;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < NSLOT; ++i) {
@@ -588,10 +602,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
           rescale = __any(grow);
         }
         if (i == NSLOT - 1) {
-          const float m_new = grow ? ceilf(xmax) : m_ref;
-          la = (int)(m_ref - m_new);
-          alpha = fast_exp2((float)la);
-          m_ref = m_new;
+          xmax_pend = xmax;
           vsplit(opaque_f(vs_next), rv_cur, sv_cur);
           eb_cur = block_exp(xmax);
           c_cur = c_next;

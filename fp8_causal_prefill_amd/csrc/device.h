@@ -137,9 +137,14 @@ __device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds) {
 }
 #pragma clang diagnostic pop
 // Wait for this wave's outstanding vector memory operations (the copies above included).
+// The wait goes through the builtin, not inline assembly, so that the compiler's own
+// counter tracking knows that every earlier load has completed and does not wait again
+// for them later (such a wait, counted without the copies, would also hold the wave for
+// loads issued after this point). Encoding: vmcnt 0, expcnt and lgkmcnt at their maxima.
 __device__ __forceinline__ void wait_vmem() {
 #if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  asm volatile("" ::: "memory");
 #endif
 }
 
