@@ -320,7 +320,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   fill_k(0, 0);
   fill_v(0, 0);
   if (n > 1) fill_k(1, 1);
-  if constexpr (FP8) {
+  {
     // the PV stage of the first iteration multiplies an all-zero P with the buffer of
     // "V_-1": make that buffer finite
 #pragma unroll
@@ -347,7 +347,6 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   float xmax0 = rowmax(sa) * c_cur;  // tile 0 always holds key 0 <= every row: finite
   float m_ref = ceilf(xmax0);
   bool rescale = false;
-  float alpha = 1.0f;
 
   // epilogue: O / l as bfloat16, and the log-sum-exp
   auto store_out = [&](float l_sum) {
@@ -649,99 +648,186 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     // O = oacc * rv_o / l
     store_out(rs_acc[0] / rv_o);
   } else {
-    // ===================== BF16: two-stage pipeline =====================
-    float l_part = 0.0f;  // this lane's half of the row sum (float32, unrounded p)
+    // ===================== BF16: three-stage pipeline =====================
+    // Iteration t: PV of tile t-1 (its P formed in iteration t-1), then the maxima of
+    // tile t with the lazy reference decision, P of tile t (bf16; float32 row sum of the
+    // unrounded values), and QK of tile t+1. P and S each live in one set of registers:
+    // P's operand tt is rewritten only after the PV products that read it, and a key
+    // group's scores only after its probabilities are formed. A reference move (rare,
+    // before any probability of tile t) scales the row sum at once and O at the top of
+    // the next iteration, once the PV of the old-unit P has been added; the factor is a
+    // power of two, exact in float32.
+    float l_part = 0.0f;   // this lane's half of the row sum
+    float o_fix = 1.0f;    // pending factor for O
+    bool o_pending = false;
+    // P of a tile: dword k packs scores 2k, 2k+1 (score i is s[i / 16][i % 16]), so the
+    // operand of PV instruction tt (keys 16 tt .. 16 tt + 15) is dwords 4 tt .. 4 tt + 3
+    v4i pw[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) pw[tt] = v4i{0, 0, 0, 0};
+    v16f (&sc)[2] = sa;  // scores of the current tile, then of the next
 
-    // One iteration t: prefetch K_{t+2}, V_{t+1}; QK of tile t+1; P and PV of tile t;
-    // maxima of tile t+1.
-    auto step = [&](auto steady_tag, int t, v16f (&s_cur)[2], v16f (&s_next)[2]) {
-      constexpr bool STEADY = decltype(steady_tag)::value;
-      const bool has_next = STEADY || t + 1 < n;
-      if (rescale) {
+    auto fix_o = [&]() {
+      if (o_pending) {
         rare_branch();
 #pragma unroll
-        for (int d = 0; d < 4; ++d) oacc[d] *= alpha;
-        l_part *= alpha;
-        rescale = false;
+        for (int d = 0; d < 4; ++d) oacc[d] *= o_fix;
+        o_fix = 1.0f;
+        o_pending = false;
       }
-      // K_{t+2} replaces K_t and V_{t+1} replaces V_{t-1}: both last read in the
-      // previous iteration
-      if constexpr (STEADY) {
-        fill_k_full(t + 2, t & 1);
-        fill_v_full(t + 1, (t + 1) & 1);
-      } else {
-        if (t + 2 < n) fill_k(t + 2, t & 1);
-        if (has_next) fill_v(t + 1, (t + 1) & 1);
+    };
+    // lazy reference decision for the tile whose row maxima (base-2 units) are xmax:
+    // m_ref moves to ceil(xmax) in rows that exceed it by more than kLazyThreshold
+    auto lazy_ref = [&](float xmax) {
+      const bool grow = xmax > m_ref + kLazyThreshold;
+      if (__any(grow)) {
+        rare_branch();
+        const float m_new = grow ? ceilf(xmax) : m_ref;
+        const float a = fast_exp2(m_ref - m_new);
+        m_ref = m_new;
+        l_part *= a;
+        o_fix *= a;
+        o_pending = true;
       }
-      if (has_next) qk((t + 1) & 1, s_next);
+    };
+    auto v_operand = [&](const char* vb, int d, int tt) {
+      const char* src = vb + d * C::KBLK + (32 * (tt >> 1) + 16 * (tt & 1)) * 64;
+      const v4bf x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)src);
+      const v4bf x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(src + 8 * 64));
+      return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    // probability of score i of the current tile
+    auto prob = [&](int i) {
+      const float pr = fast_exp2(fmaf(sc[i >> 4][i & 15], c_cur, -m_ref));
+      l_part += pr;
+      return pr;
+    };
 
-      // p = 2^(s*c - m_ref), rounded to bf16 for P V; float32 row sum
-      v8bf pbf[4];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int g = tt >> 1;
-        const int r0 = 8 * (tt & 1);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float pr = fast_exp2(fmaf(s_cur[g][r0 + j], c_cur, -m_ref));
-          l_part += pr;
-          pbf[tt][j] = (__bf16)pr;
-        }
-      }
-      // O^T += V^T P^T: keys of MFMA tt are 32(tt/2) + 16(tt%2) + 8u + 4h + r
+    // Generic iteration (the diagonal tiles and the tail), in program order.
+    auto step = [&](int t) {
+      fix_o();
+      if (t + 2 < n) fill_k(t + 2, t & 1);
       {
-        const char* vb = vring + (t & 1) * C::VBUF + v_off0;
+        const char* vb = vring + ((t + 1) & 1) * C::VBUF + v_off0;  // V of tile t-1
 #pragma unroll
         for (int d = 0; d < 4; ++d)
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            const char* src = vb + d * C::KBLK + (32 * (tt >> 1) + 16 * (tt & 1)) * 64;
-            const v4bf x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)src);
-            const v4bf x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(src + 8 * 64));
-            oacc[d] = mfma_bf16(__builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7), pbf[tt], oacc[d]);
-          }
+          for (int tt = 0; tt < 4; ++tt)
+            oacc[d] = mfma_bf16(v_operand(vb, d, tt), __builtin_bit_cast(v8bf, pw[tt]), oacc[d]);
       }
-      float xmax = 0.0f;
-      if (has_next) {
-        if constexpr (!STEADY) mask(s_next, t + 1);
-        xmax = rowmax(s_next) * c_cur;
-      }
-      if (has_next) {
-        const bool grow = xmax > m_ref + kLazyThreshold;
-        rescale = __any(grow);
-        const float m_new = grow ? ceilf(xmax) : m_ref;
-        alpha = fast_exp2(m_ref - m_new);
-        m_ref = m_new;
-      }
-      if constexpr (STEADY) {
-        // 16 QK instructions while P is formed, then 16 PV instructions with the maxima
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      mask(sc, t);
+      lazy_ref(rowmax(sc) * c_cur);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-        }
+      for (int k = 0; k < 16; ++k) {
+        const float p0 = prob(2 * k);
+        pw[k >> 2][k & 3] = (int)pack_bf16x2(p0, prob(2 * k + 1));
       }
+      if (t + 1 < n) qk((t + 1) & 1, sc);
       wait_fills();
       __syncthreads();
+      if (t + 1 < n) fill_v(t + 1, (t + 1) & 1);
     };
 
+    // Steady iteration, hand-ordered: slot i issues matrix instruction i (PV of tile t-1:
+    // dv block j % 4, key chunk j / 4 for j = i; then QK of tile t+1: key group j / NKS,
+    // head-dim chunk j % NKS for j = i - 16), fetches the LDS operand of instruction
+    // i+2, and runs one share of the vector work: the maxima of key group 1 (slots 0-1;
+    // group 0 was done at the end of the previous iteration), the lazy decision (slots
+    // 2-3), the 32 probabilities (score i in slot 4 + 5i/8: slots 4-23), and the maxima
+    // of the next tile's key group 0 (four slots from MX0_SLOT, two after its last
+    // product).
+    constexpr int NQKB = 2 * C::NKS;
+    constexpr int NSLOTB = 16 + NQKB;
+    constexpr int MX0_SLOT = 16 + C::NKS + 1;
+    static_assert(C::NKS == 8 || C::NKS == 12, "BF16 slot plan");
+    // steady iterations: tile t unmasked in every row of the workgroup, K_{t+2} a full
+    // tile within S, and a next tile
+    const int n_steady_b = max(0, min(q0_wg / C::BN, min(S / C::BN - 2, n - 1)));
+    float mx0 = -INFINITY;  // row maxima of the current tile's key group 0 (this lane's half)
+    auto steady_step = [&](int t) {
+      fix_o();
+      fill_k_full(t + 2, t & 1);
+      const char* kb = kring + ((t + 1) & 1) * C::KBUF;           // K of tile t+1
+      const char* vb = vring + ((t + 1) & 1) * C::VBUF + v_off0;  // V of tile t-1
+      auto read_op = [&](int i) -> v8bf {
+        if (i < 16) return v_operand(vb, i & 3, i >> 2);
+        const int j = i - 16, g = j / C::NKS, c = j % C::NKS;
+        return *(const v8bf*)(kb + (c >> 1) * C::KBLK + 32 * g * 64 + ((c & 1) ? k_off1 : k_off0));
+      };
+      v8bf op[3];
+      op[0] = read_op(0);
+      op[1] = read_op(1);
+      float mx = mx0, xmax = 0.0f, p_even = 0.0f;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma clang loop unroll(full)
+      for (int i = 0; i < NSLOTB; ++i) {
+        if (i + 2 < NSLOTB) op[(i + 2) % 3] = read_op(i + 2);
+        if (i < 2) {
+#pragma unroll
+          for (int r = 8 * i; r < 8 * i + 8; ++r) mx = fmaxf(mx, sc[1][r]);
+        }
+        if (i == 2) xmax = max_across_halves(mx) * c_cur;
+#pragma clang loop unroll(full)
+        for (int k = 0; k < 32; ++k) {
+          if (4 + ((5 * k) >> 3) == i) {
+            const float pr = prob(k);
+            if (k & 1) {
+              pw[k >> 3][(k >> 1) & 3] = (int)pack_bf16x2(p_even, pr);
+              keep_here(pw[k >> 3]);
+            } else {
+              p_even = pr;
+            }
+          }
+        }
+        if (i >= MX0_SLOT && i < MX0_SLOT + 4) {
+          if (i == MX0_SLOT) mx0 = -INFINITY;
+#pragma unroll
+          for (int r = 4 * (i - MX0_SLOT); r < 4 * (i - MX0_SLOT) + 4; ++r) mx0 = fmaxf(mx0, sc[0][r]);
+        }
+        if (i < 16) {
+          oacc[i & 3] = mfma_bf16(op[i % 3], __builtin_bit_cast(v8bf, pw[i >> 2]), oacc[i & 3]);
+        } else {
+          const int j = i - 16, g = j / C::NKS, c = j % C::NKS;
+          // (a group's first product starts from zero: no register clearing)
+          sc[g] = mfma_bf16(op[i % 3], qreg[c], c == 0 ? v16f{0} : sc[g]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (i == 3) {
+          lazy_ref(xmax);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // the products of this iteration stay in its slots (the next iteration's O fix is a
+      // branch, and the compiler would otherwise sink them past it)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) keep_here(oacc[d]);
+      wait_fills();
+      __syncthreads();
+      // V_{t+1} replaces V_{t-1}, last read by this iteration's PV products
+      fill_v_full(t + 1, (t + 1) & 1);
+    };
+
+    // the tile-0 scores are in sc (masked); the steady iterations need the maxima of
+    // their tile's key group 0 on entry
+    {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx0 = fmaxf(mx0, sc[0][r]);
+    }
     int t = 0;
-    for (; t < n_steady; t += 2) {
-      step(std::true_type{}, t, sa, sb);
-      step(std::true_type{}, t + 1, sb, sa);
+    for (; t < n_steady_b; ++t) steady_step(t);
+    for (; t < n; ++t) step(t);
+    // drain: PV of the last tile
+    fix_o();
+    {
+      const char* vb = vring + ((n - 1) & 1) * C::VBUF + v_off0;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          oacc[d] = mfma_bf16(v_operand(vb, d, tt), __builtin_bit_cast(v8bf, pw[tt]), oacc[d]);
     }
-    for (; t < n; t += 2) {
-      step(std::false_type{}, t, sa, sb);
-      if (t + 1 < n) step(std::false_type{}, t + 1, sb, sa);
-    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) pin_acc(oacc[d]);
     store_out(sum_across_halves(l_part));
   }
 }

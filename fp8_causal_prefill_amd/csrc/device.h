@@ -171,9 +171,10 @@ __device__ __forceinline__ int cvt_pk_fp8(float a, float b, int old) {
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  // (__bf16) conversion is round-to-nearest-even on gfx950 (v_cvt_pk_bf16_f32).
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  // one v_cvt_pk_bf16_f32 (round-to-nearest-even): a in the low half, b in the high half
+  typedef float v2f_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f_t){a, b}, v2bf_t));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
