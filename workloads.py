@@ -69,6 +69,12 @@ def _rng(w: Workload, tensor_id: int, seed: int):
     return np.random.default_rng([w.wid, tensor_id, seed])
 
 
+# the "rising" distribution: logit growth per 64 keys (base 2) and the query's weight on
+# the shared direction
+RISE_BINADES = 5.0
+RISE_A = 8.0
+
+
 def generate(w: Workload, seed: int = 0):
     """Float32 Q [B, Hq, S, Dqk], K [B, Hkv, S, Dqk], V [B, Hkv, S, Dv]."""
     q = _rng(w, 0, seed).standard_normal((w.B, w.Hq, w.S, w.Dqk), dtype=np.float32)
@@ -80,6 +86,17 @@ def generate(w: Workload, seed: int = 0):
         k[..., channels] *= np.float32(15.0)
         offset = _rng(w, 4, seed).normal(0.0, math.sqrt(2.0), size=(w.B, w.Hkv, 1, w.Dqk)).astype(np.float32)
         k += offset
+    elif w.dist == "rising":
+        # Scores that climb along the key axis: q_i . k_j carries a term A * RISE_B * j
+        # along one random unit direction per KV head, so that with the softmax scale
+        # 1/sqrt(Dqk) the base-2 logits gain about RISE_BINADES per 64 keys and every
+        # row's running maximum keeps growing (stress input for the online softmax).
+        tau_log2e = math.log2(math.e) / math.sqrt(w.Dqk)
+        slope = RISE_BINADES / (64.0 * tau_log2e * RISE_A)
+        u = _rng(w, 3, seed).standard_normal((w.B, w.Hkv, 1, w.Dqk))
+        u /= np.linalg.norm(u, axis=-1, keepdims=True)
+        q += (RISE_A * np.repeat(u, w.Hq // w.Hkv, axis=1)).astype(np.float32)
+        k += (slope * np.arange(w.S, dtype=np.float64)[None, None, :, None] * u).astype(np.float32)
     elif w.dist != "gaussian":
         raise ValueError(f"unknown distribution {w.dist}")
     return q, k, v
