@@ -11,12 +11,14 @@
 // precision, and the attention kernel can apply the V scale without rounding it
 // into the probabilities.
 //
-// One workgroup per (batch, head, token block). Each thread owns 8 consecutive
-// elements of a row per chunk (16-byte loads for fp32 halves, coalesced along D);
-// the block stays in registers between the absmax reduction and the conversion,
-// so HBM sees one read of x and one write of the codes. The rotation is a fast
-// Walsh-Hadamard transform: 3 butterfly stages inside a thread, 4 across the 16
-// lanes that hold one 128-wide row.
+// One workgroup per (batch, head, token block). Each thread owns chunks of 4 consecutive
+// elements of a row, consecutive lanes holding consecutive chunks, so that every wave
+// load is one contiguous 1 KiB run (fp32; 512 B for bf16) and every store of 4 codes a
+// contiguous 256 B run; both carry the nontemporal hint (x is read once, the codes are
+// read by a later kernel). The block stays in registers between the absmax reduction
+// and the conversion, so HBM sees one read of x and one write of the codes. The
+// rotation is a fast Walsh-Hadamard transform: 2 butterfly stages inside a thread, 5
+// across the 32 lanes that hold one 128-wide row.
 #include "device.h"
 #include "launch.h"
 
@@ -27,9 +29,10 @@ constexpr int kQThreads = 256;
 template <int D, int BLOCK, bool BF16IN, bool HAD>
 __global__ __launch_bounds__(kQThreads) void quantize_kernel(const void* __restrict__ x, uint8_t* __restrict__ codes,
                                                              float* __restrict__ scales, int S, int nb) {
-  constexpr int CPR = D / 8;                               // 8-element chunks per row
+  constexpr int CPR = D / 4;                                       // 4-element chunks per row
   constexpr int NCH = (BLOCK * CPR + kQThreads - 1) / kQThreads;  // chunks per thread
   static_assert(!HAD || D == 128, "rotation is defined for D = 128");
+  static_assert(BLOCK * CPR % kQThreads == 0, "chunks split evenly over the threads");
   __shared__ float red[kQThreads / 64];
 
   const int tid = threadIdx.x;
@@ -39,62 +42,56 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const void* __restr
   const int ntok = min(BLOCK, S - t0);
   const size_t base = ((size_t)bh * S + t0) * D;  // element offset of the block's first token
 
-  float vals[NCH][8];
+  float vals[NCH][4];
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = tid + i * kQThreads;
     const int row = c / CPR;
-    const int col = (c % CPR) * 8;
-    const bool valid = row < ntok;
-    if (valid) {
+    const int col = (c % CPR) * 4;
+    if (row < ntok) {
       if constexpr (BF16IN) {
-        const v4i w = *(const v4i*)((const uint16_t*)x + base + (size_t)row * D + col);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          vals[i][2 * j] = __builtin_bit_cast(float, (unsigned)w[j] << 16);
-          vals[i][2 * j + 1] = __builtin_bit_cast(float, (unsigned)w[j] & 0xFFFF0000u);
-        }
+        typedef unsigned v2u __attribute__((ext_vector_type(2)));
+        const v2u w = __builtin_nontemporal_load((const v2u*)((const uint16_t*)x + base + (size_t)row * D + col));
+        vals[i][0] = __builtin_bit_cast(float, w[0] << 16);
+        vals[i][1] = __builtin_bit_cast(float, w[0] & 0xFFFF0000u);
+        vals[i][2] = __builtin_bit_cast(float, w[1] << 16);
+        vals[i][3] = __builtin_bit_cast(float, w[1] & 0xFFFF0000u);
       } else {
-        const float* src = (const float*)x + base + (size_t)row * D + col;
-        const v4f a = *(const v4f*)src;
-        const v4f b = *(const v4f*)(src + 4);
+        const v4f a = __builtin_nontemporal_load((const v4f*)((const float*)x + base + (size_t)row * D + col));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          vals[i][j] = a[j];
-          vals[i][4 + j] = b[j];
-        }
+        for (int j = 0; j < 4; ++j) vals[i][j] = a[j];
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) vals[i][j] = 0.0f;
+      for (int j = 0; j < 4; ++j) vals[i][j] = 0.0f;
     }
     if constexpr (HAD) {
-      // stages 1, 2, 4 inside the thread (Sylvester order: the upper index gets a - b)
+      // stages 1, 2 inside the thread (Sylvester order: the upper index gets a - b)
 #pragma unroll
-      for (int s = 1; s < 8; s <<= 1)
+      for (int s = 1; s < 4; s <<= 1)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 4; ++j)
           if (!(j & s)) {
             const float a = vals[i][j], b = vals[i][j + s];
             vals[i][j] = a + b;
             vals[i][j + s] = a - b;
           }
-      // stages 8 .. 64 across the 16 lanes of the row (lane bit = element bit - 3)
+      // stages 4 .. 64 across the 32 lanes of the row (lane bit = element bit - 2)
 #pragma unroll
-      for (int s = 1; s < 16; s <<= 1) {
+      for (int s = 1; s < 32; s <<= 1) {
         const bool upper = (tid & s) != 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
           const float other = __shfl_xor(vals[i][j], s, 64);
           vals[i][j] = upper ? other - vals[i][j] : vals[i][j] + other;
         }
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) vals[i][j] *= 0.08838834764831845f;  // 1 / sqrt(128)
+      for (int j = 0; j < 4; ++j) vals[i][j] *= 0.08838834764831845f;  // 1 / sqrt(128)
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(vals[i][j]));
+    for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(vals[i][j]));
   }
 
   // block absmax
@@ -121,17 +118,13 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const void* __restr
   for (int i = 0; i < NCH; ++i) {
     const int c = tid + i * kQThreads;
     const int row = c / CPR;
-    const int col = (c % CPR) * 8;
+    const int col = (c % CPR) * 4;
     if (row < ntok) {
-      int w0 = 0, w1 = 0;
-      float y[8];
+      float y[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) y[j] = fminf(fmaxf(ldexpf(vals[i][j], -k), -448.0f), 448.0f);  // exact quotient
-      w0 = cvt_pk_fp8<false>(y[0], y[1], w0);
-      w0 = cvt_pk_fp8<true>(y[2], y[3], w0);
-      w1 = cvt_pk_fp8<false>(y[4], y[5], w1);
-      w1 = cvt_pk_fp8<true>(y[6], y[7], w1);
-      *(uint2*)(codes + base + (size_t)row * D + col) = make_uint2((unsigned)w0, (unsigned)w1);
+      for (int j = 0; j < 4; ++j) y[j] = fminf(fmaxf(ldexpf(vals[i][j], -k), -448.0f), 448.0f);  // exact quotient
+      const int w = cvt_pk_fp8<true>(y[2], y[3], cvt_pk_fp8<false>(y[0], y[1], 0));
+      __builtin_nontemporal_store((unsigned)w, (unsigned*)(codes + base + (size_t)row * D + col));
     }
   }
 }
