@@ -7,7 +7,7 @@
 //    Instructions": in FP8 the softmax needs about as many vector cycles as the
 //    matrix products need matrix cycles, and only the instruction order overlaps
 //    the two, so the loop below is software-pipelined and its schedule is fixed
-//    with scheduling-group barriers.
+//    by hand.
 //  * "Precision and Underflow of FP8 Probabilities" and "Per-Block Scaling and
 //    Normalization by the Rounded Row Sum": probabilities of each (query row,
 //    64-key block) are multiplied by a power of two that puts the block maximum in
@@ -32,15 +32,17 @@
 //    V row order) make every LDS read of a half-wave hit 64 distinct banks.
 //  * O^T = V^T P^T accumulates on the MFMA with each lane owning one query row, so
 //    rescaling O by a per-row factor is a per-lane multiply.
-//  * Pipeline per 64-key tile t: QK for tile t+1 is issued while the probabilities
-//    of tile t are formed; BF16 then multiplies P_t V_t, FP8 multiplies P_{t-1}
-//    V_{t-1} (one stage later, so that the matrix work of one iteration - 4 QK, 4
-//    PV and 1 row-sum instructions - overlaps all of the vector work); the row
-//    maxima of tile t+1 close the iteration.
+//  * Pipeline per 64-key tile t, in both precisions: the iteration that forms the
+//    probabilities of tile t also issues the QK products of tile t+1 and the PV
+//    products of tile t-1 (P_{t-1} V_{t-1}, one stage late), so that its matrix work
+//    (FP8: 4 QK, 4 PV and 1 row-sum instructions; BF16: 16 QK and 16 PV) overlaps all
+//    of its vector work. The steady iterations issue one matrix instruction per
+//    slot, with the vector work spread over the slots and sched_barrier fencing
+//    them.
 //  * The exponent reference m_ref is an integer that is raised lazily: only when a
 //    row's maximum exceeds it by more than kLazyThreshold binades are O and the row
-//    sum rescaled (by a power of two; for FP8 the in-flight probabilities of the
-//    previous tile are re-scaled exactly through their E8M0 scale).
+//    sum rescaled (by a power of two; the in-flight probabilities of the previous
+//    tile are re-scaled exactly, for FP8 through their E8M0 scale).
 //  * Causal-block skipping: a workgroup visits key tiles 0 .. (its last row) / 64;
 //    the mask is evaluated only on tiles that reach past a wave's first row.
 //  * Scheduling: workgroups are issued heaviest (last query tile) first; within a
@@ -427,7 +429,10 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
         const float p1 = fast_exp2(fmaf(sv[j0 + 1], c, -bias));
         const float p2 = fast_exp2(fmaf(sv[j0 + 2], c, -bias));
         const float p3 = fast_exp2(fmaf(sv[j0 + 3], c, -bias));
-        return cvt_pk_fp8<true>(p2, p3, cvt_pk_fp8<false>(p0, p1, 0));
+        // (the low-half conversion keeps the high half of its destination, which the
+        // second conversion overwrites: passing p0's bits there, a register that dies in
+        // this instruction, spares clearing one)
+        return cvt_pk_fp8<true>(p2, p3, cvt_pk_fp8<false>(p0, p1, __float_as_int(p0)));
       }
     };
 
@@ -479,16 +484,15 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       rs_acc = mfma_fp8_scaled(ones_fp8, pp, rs_acc, k127, sp);
     };
 
-    // One iteration t: prefetch K_{t+2}; QK of tile t+1; PV of tile t-1; P of tile t;
-    // maxima of tile t+1. STEADY iterations (t + 2 < n, no mask) have no branches
-    // between the rare unit fix at the top and the rare reference update at the end.
-    auto step = [&](auto steady_tag, int t, v16f (&s_cur)[2], v16f (&s_next)[2], v8i& p_prev, v8i& p_cur) {
-      constexpr bool STEADY = decltype(steady_tag)::value;
-      const bool has_next = STEADY || t + 1 < n;
+    // Generic iteration t (the diagonal tiles and the tail), in program order: copy
+    // K_{t+2}; QK of tile t+1; PV of tile t-1; P of tile t; maxima of tile t+1 (masked)
+    // and the lazy decision; barrier; copy V_{t+1}.
+    auto step = [&](int t, v16f (&s_cur)[2], v16f (&s_next)[2], v8i& p_prev, v8i& p_cur) {
+      const bool has_next = t + 1 < n;
       fix_units();
       const float ks_pf = kscale[sidx(t + 2)];
       const float vs_pf = vscale[sidx(t + 2)];
-      if (STEADY || t + 2 < n) fill_k(t + 2, (t + 2) % C::NBUF);
+      if (t + 2 < n) fill_k(t + 2, (t + 2) % C::NBUF);
       if (has_next) qk((t + 1) % C::NBUF, s_next);
       pv(p_prev, sp_prev, sv_prev, (t + C::NBUF - 1) % C::NBUF);
 
@@ -508,7 +512,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
 
       float xmax = 0.0f, c_next = c_cur;
       if (has_next) {
-        if constexpr (!STEADY) mask(s_next, t + 1);
+        mask(s_next, t + 1);
         c_next = c_q * ks_next;
         xmax = rowmax(s_next) * c_next;
       }
@@ -636,8 +640,8 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       steady_step(t + 1, sb, sa, pb, pa);
     }
     for (; t < n; t += 2) {
-      step(std::false_type{}, t, sa, sb, pa, pb);
-      if (t + 1 < n) step(std::false_type{}, t + 1, sb, sa, pb, pa);
+      step(t, sa, sb, pa, pb);
+      if (t + 1 < n) step(t + 1, sb, sa, pb, pa);
     }
     // drain: PV of the last tile (its P is pb if n - 1 is even, else pa)
     fix_units();
