@@ -20,7 +20,7 @@
 //    e4m3 code as a linear function of x (the page's lean P).
 //
 // Work decomposition (one workgroup = 32 query rows per wave of one head: 8 waves,
-// one workgroup per CU, for FP8 at D = 128; 4 waves, two workgroups per CU otherwise;
+// one workgroup per CU; 4 waves, two workgroups per CU, for FP8 at Dqk = 192;
 // always two waves per SIMD):
 //  * Each wave owns 32 query rows and computes S^T = K Q^T on 32x32 MFMA tiles,
 //    so every lane holds the scores of one query row (lane % 32) for half of the
@@ -67,9 +67,10 @@ constexpr float kLeanBias = 56.0f - 0.46f;
 template <bool FP8, int DQK>
 struct Cfg {
   static constexpr int DV = 128;
-  // FP8 at D = 128: eight waves (256 query rows share each K/V tile copy, halving the
-  // copy traffic that competes with the operand reads for LDS); otherwise four
-  static constexpr int WAVES = (FP8 && DQK == 128) ? 8 : 4;
+  // Eight waves (256 query rows share each K/V tile copy, halving the copy traffic per
+  // FLOP) wherever a tile splits evenly into 16-byte copies of all 512 threads: all but
+  // the FP8 K tile of the 192-wide head (12 KiB), which keeps four
+  static constexpr int WAVES = (FP8 && DQK != 128) ? 4 : 8;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;  // query rows per workgroup
   static constexpr int BN = 64;          // keys per tile
