@@ -20,8 +20,7 @@
 //    e4m3 code as a linear function of x (the page's lean P).
 //
 // Work decomposition (one workgroup = 32 query rows per wave of one head: 8 waves,
-// one workgroup per CU; 4 waves, two workgroups per CU, for FP8 at Dqk = 192;
-// always two waves per SIMD):
+// one workgroup per CU, two waves per SIMD):
 //  * Each wave owns 32 query rows and computes S^T = K Q^T on 32x32 MFMA tiles,
 //    so every lane holds the scores of one query row (lane % 32) for half of the
 //    keys of a tile; row maxima need one lane-half exchange (v_permlane32_swap).
@@ -67,10 +66,9 @@ constexpr float kLeanBias = 56.0f - 0.46f;
 template <bool FP8, int DQK>
 struct Cfg {
   static constexpr int DV = 128;
-  // Eight waves (256 query rows share each K/V tile copy, halving the copy traffic per
-  // FLOP) wherever a tile splits evenly into 16-byte copies of all 512 threads: all but
-  // the FP8 K tile of the 192-wide head (12 KiB), which keeps four
-  static constexpr int WAVES = (FP8 && DQK != 128) ? 4 : 8;
+  // Eight waves: 256 query rows share each K/V tile copy, halving the copy traffic per
+  // FLOP against four
+  static constexpr int WAVES = 8;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;  // query rows per workgroup
   static constexpr int BN = 64;          // keys per tile
@@ -91,11 +89,15 @@ struct Cfg {
   // LDS ring depth per tensor: two buffers, one barrier per iteration
   static constexpr int NBUF = 2;
   static constexpr int LDS_BYTES = NBUF * (KBUF + VBUF);
-  static constexpr int KCHUNKS = BN * KROW / 16 / THREADS;  // 16-byte loads per thread per tile
-  static constexpr int VCHUNKS = BN * VROW / 16 / THREADS;
+  // 16-byte copies per tile, and per thread (rounded up: a tile that does not split
+  // evenly over the threads leaves whole waves idle in its last round)
+  static constexpr int KSLOTS = BN * KROW / 16;
+  static constexpr int VSLOTS = BN * VROW / 16;
+  static constexpr int KCHUNKS = (KSLOTS + THREADS - 1) / THREADS;
+  static constexpr int VCHUNKS = (VSLOTS + THREADS - 1) / THREADS;
   static constexpr int KSTEP = FP8 ? 64 : 16;  // MFMA reduction depth
   static constexpr int NKS = DQK / KSTEP;
-  static_assert(BN * KROW % (16 * THREADS) == 0 && BN * VROW % (16 * THREADS) == 0, "tile load split");
+  static_assert(KSLOTS % 64 == 0 && VSLOTS % 64 == 0, "tile copies split into whole waves");
   static_assert(DQK % KSTEP == 0, "head dim must divide the MFMA depth");
   static_assert(BM % (2 * BN) == 0, "steady iterations rely on an even number of key tiles per query tile");
 };
@@ -187,6 +189,10 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   // within a tile does not depend on the tile; only the last tile of a sequence whose
   // length is not a multiple of BN clamps its rows to S - 1.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // does this wave copy chunk i of a tile (always, unless the tile's last round of
+  // copies does not reach every wave)?
+  auto k_live = [&](int i) { return (i + 1) * C::THREADS <= C::KSLOTS || wave_u * 64 + i * C::THREADS < C::KSLOTS; };
+  auto v_live = [&](int i) { return (i + 1) * C::THREADS <= C::VSLOTS || wave_u * 64 + i * C::THREADS < C::VSLOTS; };
   auto k_pos_row = [&](int i) { return ((tid + i * C::THREADS) >> 2) % C::BN; };
   auto k_pos_off = [&](int i) {  // bytes within the K row
     const int pos = tid + i * C::THREADS;
@@ -215,12 +221,13 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     if (t0 + C::BN <= S) {
       const char* tile = kbase + (size_t)t0 * C::KROW;
 #pragma unroll
-      for (int i = 0; i < C::KCHUNKS; ++i) lds_copy16(tile, k_src[i], dst + i * C::THREADS * 16);
+      for (int i = 0; i < C::KCHUNKS; ++i)
+        if (k_live(i)) lds_copy16(tile, k_src[i], dst + i * C::THREADS * 16);
     } else {
 #pragma unroll
       for (int i = 0; i < C::KCHUNKS; ++i) {
         const int gr = min(t0 + k_pos_row(i), S - 1);
-        lds_copy16(kbase + (size_t)gr * C::KROW + k_pos_off(i), dst + i * C::THREADS * 16);
+        if (k_live(i)) lds_copy16(kbase + (size_t)gr * C::KROW + k_pos_off(i), dst + i * C::THREADS * 16);
       }
     }
   };
@@ -230,12 +237,13 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     if (t0 + C::BN <= S) {
       const char* tile = vbase + (size_t)t0 * C::VROW;
 #pragma unroll
-      for (int i = 0; i < C::VCHUNKS; ++i) lds_copy16(tile, v_src[i], dst + i * C::THREADS * 16);
+      for (int i = 0; i < C::VCHUNKS; ++i)
+        if (v_live(i)) lds_copy16(tile, v_src[i], dst + i * C::THREADS * 16);
     } else {
 #pragma unroll
       for (int i = 0; i < C::VCHUNKS; ++i) {
         const int gr = min(t0 + v_pos_row(i), S - 1);
-        lds_copy16(vbase + (size_t)gr * C::VROW + v_pos_off(i), dst + i * C::THREADS * 16);
+        if (v_live(i)) lds_copy16(vbase + (size_t)gr * C::VROW + v_pos_off(i), dst + i * C::THREADS * 16);
       }
     }
   };
@@ -244,13 +252,15 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     const char* tile = kbase + (size_t)(t * C::BN) * C::KROW;
     const uint32_t dst = k_lds + buf * C::KBUF + wave_u * 64 * 16;
 #pragma unroll
-    for (int i = 0; i < C::KCHUNKS; ++i) lds_copy16(tile, k_src[i], dst + i * C::THREADS * 16);
+    for (int i = 0; i < C::KCHUNKS; ++i)
+      if (k_live(i)) lds_copy16(tile, k_src[i], dst + i * C::THREADS * 16);
   };
   auto fill_v_full = [&](int t, int buf) {
     const char* tile = vbase + (size_t)(t * C::BN) * C::VROW;
     const uint32_t dst = v_lds + buf * C::VBUF + wave_u * 64 * 16;
 #pragma unroll
-    for (int i = 0; i < C::VCHUNKS; ++i) lds_copy16(tile, v_src[i], dst + i * C::THREADS * 16);
+    for (int i = 0; i < C::VCHUNKS; ++i)
+      if (v_live(i)) lds_copy16(tile, v_src[i], dst + i * C::THREADS * 16);
   };
   // make this wave's copies complete before the barrier that publishes them
   auto wait_fills = [] { wait_vmem(); };
@@ -328,7 +338,8 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     // "V_-1": make that buffer finite
 #pragma unroll
     for (int i = 0; i < C::VCHUNKS; ++i)
-      *(v4i*)(vring + (C::NBUF - 1) * C::VBUF + (tid + i * C::THREADS) * 16) = v4i{0, 0, 0, 0};
+      if (tid + i * C::THREADS < C::VSLOTS)
+        *(v4i*)(vring + (C::NBUF - 1) * C::VBUF + (tid + i * C::THREADS) * 16) = v4i{0, 0, 0, 0};
   }
   wait_fills();
   __syncthreads();
