@@ -381,8 +381,6 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
 
   if constexpr (FP8) {
     // ===================== FP8: three-stage pipeline =====================
-    const v8i ones_fp8 = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                          0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
     const int k127 = opaque(kE8M0One);
 
     // V scale = rv * 2^ev, rv in [1, 2): 2^ev is the V operand's E8M0 scale (exact);
@@ -493,7 +491,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
         const v8i a = {va[0], va[1], va[2], va[3], va[4], va[5], va[6], va[7]};
         oacc[d] = mfma_fp8_scaled(a, pp, oacc[d], svr, sp);
       }
-      rs_acc = mfma_fp8_scaled(ones_fp8, pp, rs_acc, k127, sp);
+      rs_acc = mfma_ones_fp4_by_fp8(pp, rs_acc, k127, sp);
     };
 
     // Generic iteration t (the diagonal tiles and the tail), in program order: copy
@@ -627,7 +625,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
         else if (i < NQK + 4)
           oacc[i - NQK] = mfma_fp8_scaled(op[i % 3], p_prev, oacc[i - NQK], svr, sp);
         else
-          rs_acc = mfma_fp8_scaled(ones_fp8, p_prev, rs_acc, k127, sp);
+          rs_acc = mfma_ones_fp4_by_fp8(p_prev, rs_acc, k127, sp);
         __builtin_amdgcn_sched_barrier(0);
       }
       // the products of this iteration stay in its slots (the next iteration's unit fix

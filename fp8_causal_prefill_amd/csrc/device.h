@@ -48,6 +48,16 @@ __device__ __forceinline__ v16f mfma_fp8_scaled(const v8i& a, const v8i& b, cons
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
 }
 
+// D += 1 * B per row of A: A is all ones in fp4 (e2m1, format 4 of the instruction's A
+// operand: 1.0 is the nibble 0b0010, so every byte is 0x22 and the 64 reduction values of
+// a lane take four registers), B e4m3 with E8M0 scale scale_b; scale_a is the E8M0 code
+// 127 (1.0), passed in a register. Every output row is the column sums of B times
+// 2^(scale_b - 127), exactly (products of 1.0 and e4m3 values).
+__device__ __forceinline__ v16f mfma_ones_fp4_by_fp8(const v8i& b, const v16f& c, int scale_a, int scale_b) {
+  const v8i ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};  // upper half unread
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, b, c, 4, 0, 0, scale_a, 0, scale_b);
+}
+
 // D += A * B on e4m3, no scaling.
 __device__ __forceinline__ v16f mfma_fp8(const v8i& a, const v8i& b, const v16f& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
