@@ -318,6 +318,15 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
           if (kt + 32 * g + 8 * (r >> 2) + 4 * h + (r & 3) > my_q) s[g][r] = -INFINITY;
     }
   };
+  // the same mask, branch-free (one compare and one select per score): for steady
+  // iterations over the diagonal tiles, where a branch would split the slot schedule
+  auto mask_nb = [&](v16f (&s)[2], int t) {
+    const int lim = my_q - t * C::BN - 4 * h;  // key offsets within the tile up to lim stay
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[g][r] = (32 * g + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[g][r];
+  };
   auto rowmax = [&](const v16f (&s)[2]) {
     float m0 = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
@@ -547,7 +556,11 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     // and runs one 64-cycle share of the vector work (4 exponentials and 2 conversions of
     // tile t's probabilities, or the maxima of tile t+1 once its scores are complete).
     // sched_barrier keeps each slot's instructions in place.
-    auto steady_step = [&](int t, v16f (&s_cur)[2], v16f (&s_next)[2], v8i& p_prev, v8i& p_cur) {
+    // MASKED: the same schedule over the diagonal tiles (any iteration with a next tile):
+    // tile t+1's scores are masked before its maxima, and the copies clamp to the
+    // sequence (K_{t+2} only if it exists).
+    auto steady_step = [&](auto masked_tag, int t, v16f (&s_cur)[2], v16f (&s_next)[2], v8i& p_prev, v8i& p_cur) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
       constexpr int NQK = 2 * C::NKS;
       constexpr int NSLOT = NQK + 5;
       fix_units();
@@ -578,7 +591,11 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       const float vs_pf = vscale[sidx(t + 2)];
       read_op(0, op[0]);
       read_op(1, op[1]);
-      fill_k_full(t + 2, (t + 2) % C::NBUF);
+      if constexpr (MASKED) {
+        if (t + 2 < n) fill_k(t + 2, (t + 2) % C::NBUF);
+      } else {
+        fill_k_full(t + 2, (t + 2) % C::NBUF);
+      }
       s_next[0] = v16f{0};
       s_next[1] = v16f{0};
       // tile t's values, before the update for tile t+1 inside the slots replaces them
@@ -601,6 +618,9 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
         // the scores of tile t+1 are complete one slot after the last QK instruction:
         // row maxima in slots NSLOT-4 and NSLOT-3, then the lazy reference update for
         // tile t+1 in the last two slots, beside the PV and row-sum instructions
+        if constexpr (MASKED) {
+          if (i == NSLOT - 4) mask_nb(s_next, t + 1);
+        }
         if (i == NSLOT - 4 || i == NSLOT - 3) {
           const int r0 = i == NSLOT - 4 ? 0 : 8;
 #pragma unroll
@@ -641,13 +661,22 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       wait_fills();
       __syncthreads();
       // V_{t+1} replaces V_{t-1}, last read by this iteration's PV products
-      fill_v_full(t + 1, (t + 1) % C::NBUF);
+      if constexpr (MASKED) {
+        fill_v(t + 1, (t + 1) % C::NBUF);
+      } else {
+        fill_v_full(t + 1, (t + 1) % C::NBUF);
+      }
     };
 
     int t = 0;
     for (; t < n_steady; t += 2) {
-      steady_step(t, sa, sb, pa, pb);
-      steady_step(t + 1, sb, sa, pb, pa);
+      steady_step(std::false_type{}, t, sa, sb, pa, pb);
+      steady_step(std::false_type{}, t + 1, sb, sa, pb, pa);
+    }
+    // the diagonal tiles, in pairs while both iterations of a pair have a next tile
+    for (; t + 2 < n; t += 2) {
+      steady_step(std::true_type{}, t, sa, sb, pa, pb);
+      steady_step(std::true_type{}, t + 1, sb, sa, pb, pa);
     }
     for (; t < n; t += 2) {
       step(t, sa, sb, pa, pb);
