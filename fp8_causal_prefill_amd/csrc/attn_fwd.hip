@@ -787,9 +787,18 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     // tile within S, and a next tile
     const int n_steady_b = max(0, min(q0_wg / C::BN, min(S / C::BN - 2, n - 1)));
     float mx0 = -INFINITY;  // row maxima of the current tile's key group 0 (this lane's half)
-    auto steady_step = [&](int t) {
+    // MASKED: the same schedule over the diagonal tiles (any iteration with a next tile):
+    // tile t's scores are masked in slot 0 and its maxima taken over both key groups
+    // there (the group-0 maxima carried from the previous iteration were unmasked); the
+    // copies clamp to the sequence (K_{t+2} only if it exists).
+    auto steady_step = [&](auto masked_tag, int t) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
       fix_o();
-      fill_k_full(t + 2, t & 1);
+      if constexpr (MASKED) {
+        if (t + 2 < n) fill_k(t + 2, t & 1);
+      } else {
+        fill_k_full(t + 2, t & 1);
+      }
       const char* kb = kring + ((t + 1) & 1) * C::KBUF;           // K of tile t+1
       const char* vb = vring + ((t + 1) & 1) * C::VBUF + v_off0;  // V of tile t-1
       auto read_op = [&](int i) -> v8bf {
@@ -800,14 +809,20 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       v8bf op[3];
       op[0] = read_op(0);
       op[1] = read_op(1);
-      float mx = mx0, xmax = 0.0f, p_even = 0.0f;
+      float mx = MASKED ? -INFINITY : mx0, xmax = 0.0f, p_even = 0.0f;
       __builtin_amdgcn_sched_barrier(0);
 #pragma clang loop unroll(full)
       for (int i = 0; i < NSLOTB; ++i) {
         if (i + 2 < NSLOTB) op[(i + 2) % 3] = read_op(i + 2);
+        if constexpr (MASKED) {
+          if (i == 0) mask_nb(sc, t);
+        }
         if (i < 2) {
 #pragma unroll
-          for (int r = 8 * i; r < 8 * i + 8; ++r) mx = fmaxf(mx, sc[1][r]);
+          for (int r = 8 * i; r < 8 * i + 8; ++r) {
+            mx = fmaxf(mx, sc[1][r]);
+            if constexpr (MASKED) mx = fmaxf(mx, sc[0][r]);
+          }
         }
         if (i == 2) xmax = max_across_halves(mx) * c_cur;
 #pragma clang loop unroll(full)
@@ -847,7 +862,11 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       wait_fills();
       __syncthreads();
       // V_{t+1} replaces V_{t-1}, last read by this iteration's PV products
-      fill_v_full(t + 1, (t + 1) & 1);
+      if constexpr (MASKED) {
+        fill_v(t + 1, (t + 1) & 1);
+      } else {
+        fill_v_full(t + 1, (t + 1) & 1);
+      }
     };
 
     // the tile-0 scores are in sc (masked); the steady iterations need the maxima of
@@ -857,7 +876,8 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       for (int r = 0; r < 16; ++r) mx0 = fmaxf(mx0, sc[0][r]);
     }
     int t = 0;
-    for (; t < n_steady_b; ++t) steady_step(t);
+    for (; t < n_steady_b; ++t) steady_step(std::false_type{}, t);
+    for (; t + 1 < n; ++t) steady_step(std::true_type{}, t);  // the diagonal tiles
     for (; t < n; ++t) step(t);
     // drain: PV of the last tile
     fix_o();
