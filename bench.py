@@ -15,6 +15,11 @@ datasheet dense FP8 peak in ``roofline``; the opt-in lean-probability FP8 mode i
 reported in ``fp8_lean`` and BF16 in ``bf16``. The CPU baseline times the fp64 oracle
 on a bounded sample (whole query heads, about 15 s) on the host cores; the heads it
 computed also give a full-size parity figure (``sampled_rel_l2_fp8``).
+
+``sustained`` runs each headline kernel back to back for a few seconds after the clock
+has settled and reports, next to its time, the median shader clock, the socket power,
+the energy per call and the fraction of the window the board spent at its power limit
+(amdsmi telemetry; null with the reason when the driver does not provide it).
 """
 
 import argparse
@@ -120,6 +125,108 @@ def time_kernel(fn, steps, warmup, stream, torch):
     return float(np.mean(ms)), float(np.median(ms))
 
 
+class Telemetry:
+    """Shader clock, socket power and energy of the GPU behind cuda:0, read from the
+    driver's metrics table through amdsmi (ZYFA, "Throughput on Captured Activations at
+    Sustained Clocks": the clock a kernel settles to under the board's power limit decides
+    its throughput, so it is reported next to it). The table refreshes about once a
+    second, so readings are taken over windows of a few seconds."""
+
+    def __init__(self, torch):
+        self.smi = None
+        self.error = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            handle = handles[0] if len(handles) == 1 else None
+            props = torch.cuda.get_device_properties(0)
+            bus = getattr(props, "pci_bus_id", None)
+            if bus is not None:
+                for h in handles:  # match cuda:0 to its PCI address when the driver lists several GPUs
+                    bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                    if int(bdf.split(":")[1], 16) == int(bus) and int(bdf.split(":")[0], 16) == int(
+                            getattr(props, "pci_domain_id", 0)):
+                        handle = h
+            if handle is None:
+                raise RuntimeError(f"cannot tell which of {len(handles)} GPUs is cuda:0")
+            self.smi, self.h = amdsmi, handle
+            self.power_limit_w = amdsmi.amdsmi_get_power_info(handle).get("power_limit", 0) / 1e6
+        except Exception as e:  # telemetry is optional: the bench line records why it is missing
+            self.error = repr(e)
+
+    def read(self):
+        m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
+        e = self.smi.amdsmi_get_energy_count(self.h)
+        clks = [c for c in m.get("current_gfxclks", []) if isinstance(c, int) and c > 0]
+        return {"gfxclk": float(np.mean(clks)) if clks else None,
+                "energy_j": e["energy_accumulator"] * e["counter_resolution"] * 1e-6,
+                "ts_ns": e["timestamp"],  # the energy reading's own time stamp, nanoseconds
+                "ppt": m.get("ppt_residency_acc"), "thm": m.get("socket_thm_residency_acc"),
+                "acc": m.get("accumulation_counter")}
+
+
+def sustained(tel, fn, flops, peak, settle_s, window_s, stream, torch):
+    """Run fn back to back: settle_s seconds for the clock to reach its steady state under
+    the power limit, then window_s seconds timed with HIP events on the kernel's stream
+    while the telemetry is sampled. Power, clock and the power-limited fraction are taken
+    between the first and the last refresh of the metrics table inside the window (readings
+    between refreshes repeat the previous one). Returns the kernel time, throughput, median
+    shader clock, mean socket power, energy per call and the fraction of the window that the
+    board spent held at its power limit (or its thermal limit)."""
+    import threading
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            samples.append(tel.read())
+            stop.wait(0.02)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    ev = []
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < window_s:
+        for _ in range(10):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    ms = float(np.mean([x.elapsed_time(y) for x, y in ev]))
+    rec = {"calls": len(ev), "ms": ms, "tflops": flops / ms / 1e9, "frac": flops / ms / 1e9 / peak,
+           "power_limit_w": tel.power_limit_w}
+    # distinct table refreshes, skipping the first reading (taken before the window's launches)
+    fresh = []
+    for s in samples[1:]:
+        if not fresh or s["ts_ns"] != fresh[-1]["ts_ns"]:
+            fresh.append(s)
+    if fresh and fresh[0]["ts_ns"] == samples[0]["ts_ns"]:
+        fresh = fresh[1:]
+    rec["refreshes"] = len(fresh)
+    clks = [s["gfxclk"] for s in fresh if s["gfxclk"] is not None]
+    rec["gfxclk_mhz_median"] = float(np.median(clks)) if clks else None
+    if len(fresh) >= 2:
+        a, b = fresh[0], fresh[-1]
+        watts = (b["energy_j"] - a["energy_j"]) / ((b["ts_ns"] - a["ts_ns"]) * 1e-9)
+        rec["socket_power_w"] = watts
+        rec["energy_per_call_j"] = watts * ms * 1e-3
+        if None not in (a["ppt"], b["ppt"], a["acc"], b["acc"]) and b["acc"] > a["acc"]:
+            rec["power_limited_fraction"] = (b["ppt"] - a["ppt"]) / (b["acc"] - a["acc"])
+            if a["thm"] is not None and b["thm"] is not None:
+                rec["thermal_limited_fraction"] = (b["thm"] - a["thm"]) / (b["acc"] - a["acc"])
+    return rec
+
+
 def other_workloads(names, steps, warmup, torch, zy):
     """Kernel throughput on the other benchmark shapes (4K MHA, 32K MLA, 16K activation-like
     with and without the Hadamard rotation of Q and K): FP8 exact and lean, and BF16.
@@ -170,6 +277,9 @@ def main():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-lean", action="store_true", help="skip the lean-probability FP8 mode")
     ap.add_argument("--no-others", action="store_true", help="skip the other workload shapes")
+    ap.add_argument("--sustain", type=float, default=4.0,
+                    help="seconds of back-to-back launches per headline kernel, after 1.5 s of settling, "
+                         "with clock and power telemetry (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -299,6 +409,27 @@ def main():
                 "peak": PEAK_BF16, "steps": bsteps, "step_ms": bstep_s * 1e3,
                 "hbm_traffic": hbm_traffic(w.name, "bf16")}
 
+    # ---------------- sustained clocks: telemetry while each kernel runs back to back ----------------
+    sustained_rec = None
+    if args.sustain > 0:
+        tel = Telemetry(torch)
+        if tel.smi is None:
+            sustained_rec = {"error": tel.error}
+        else:
+            sustained_rec = {"settle_s": 1.5, "window_s": args.sustain}
+            kernels = [("fp8", lambda: zy.attn_fwd_fp8(qc, kc, vc, qs, ks, vs, blk, scale, o=o8), PEAK_FP8)]
+            if not args.no_lean:
+                kernels.append(("fp8_lean", lambda: zy.attn_fwd_fp8(qc, kc, vc, qs, ks, vs, blk, scale, o=o8l,
+                                                                    lean=True), PEAK_FP8))
+            if not args.no_bf16:
+                kernels.append(("bf16", lambda: zy.attn_fwd_bf16(qb, kb, vb, scale, o=ob), PEAK_BF16))
+            for name, fn, peak in kernels:
+                sustained_rec[name] = sustained(tel, fn, flops, peak, 1.5, args.sustain, stream, torch)
+                r = sustained_rec[name]
+                print(f"[bench] sustained {name}: {r['ms']:.3f} ms, {r['frac'] * 100:.1f}% of peak, "
+                      f"clock {r['gfxclk_mhz_median']} MHz, power {r.get('socket_power_w')} W", file=sys.stderr,
+                      flush=True)
+
     achieved = flops / attn_s / 1e12
     line = {
         "metric": "causal prefill attn TFLOPS + % of FP8 MFMA peak, S=32K D=128 (FP8 & BF16)",
@@ -323,6 +454,7 @@ def main():
                      "kernel_ms_median": attn_med_s * 1e3},
         "fp8_lean": lean,
         "bf16": bf16,
+        "sustained": sustained_rec,
     }
 
     if not args.no_others:
