@@ -20,6 +20,9 @@ Sources (cited by page title and section):
   - footnote 7 and "Precision and Underflow of FP8 Probabilities": the e4m3
     code points and thresholds.
   - "Methodology and Limitations": equal query and key lengths.
+* Zyphra "Inference Wave 2", section on CSA dual-scope decode: keys split
+  into shards, each returning a partial output and its log-sum-exp, merged
+  into the result of one pass.
 * The FP8 GEMM on CDNA4 practitioner's blog (kwkr.cn), sections 2.1-2.3:
   e4m3 range (max 448), absmax block scaling with a zero guard, and
   round-to-nearest-even.
@@ -31,7 +34,9 @@ Modules:
 * ``quant``     - per-(batch, head, token-block) absmax quantizer and the
                   Sylvester Hadamard rotation.
 * ``attention`` - fp64 causal attention with GQA and log-sum-exp, over all
-                  rows or a chosen subset of query rows.
+                  rows or a chosen subset of query rows; the same for a chunk of
+                  query rows against a window of keys, and the merge of partial
+                  results over disjoint key sets.
 
 Every function here is pinned by tests that do not re-derive it from itself:
 printed code points, closed forms, invariants, brute force in 50-digit
@@ -42,10 +47,10 @@ Hadamard matrix, torch's float64 scaled_dot_product_attention).
 from .fp8 import (E4M3_MAX, e4m3_decode, e4m3_encode, bf16_round, bf16_bits_to_f64,
                   f32_to_bf16_bits)
 from .quant import quantize_blocks, dequantize_blocks, hadamard_matrix, hadamard_rotate
-from .attention import causal_attention, causal_probs
+from .attention import causal_attention, causal_probs, merge_partials, window_attention
 
 __all__ = [
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "bf16_round", "bf16_bits_to_f64", "f32_to_bf16_bits",
     "quantize_blocks", "dequantize_blocks", "hadamard_matrix", "hadamard_rotate",
-    "causal_attention", "causal_probs",
+    "causal_attention", "causal_probs", "window_attention", "merge_partials",
 ]

@@ -73,3 +73,73 @@ def causal_attention(q, k, v, scale, rows=None, row_chunk=256):
                 o[b, h, c0:c0 + len(idx)] = (w @ v[b, g, :n]) / l[:, None]
                 lse[b, h, c0:c0 + len(idx)] = m + np.log(l)
     return o, lse
+
+
+def window_attention(q, k, v, scale, q_offset=0, k_begin=0, k_end=None, rows=None, row_chunk=256):
+    """Causal attention of a chunk of query rows against a window of keys, in float64.
+
+    Zyphra "Inference Wave 2", section on CSA dual-scope decode: the keys of one call may
+    be split into shards, each giving a partial output and the log-sum-exp of its scores;
+    the ZYFA Introduction fixes the causal rule (a query sees keys up to its own position).
+
+    q: [B, Hq, Sq, Dqk], query row i being the token at sequence position q_offset + i.
+    k: [B, Hkv, Skv, Dqk], v: [B, Hkv, Skv, Dv], key j being the token at position j.
+    Key j is visible to row i iff k_begin <= j < k_end and j <= q_offset + i (k_end
+    defaults to Skv). Over the visible keys, O_i and LSE_i are as in causal_attention; a
+    row with no visible key has O_i = 0 and LSE_i = -inf (a part that holds none of the
+    row's keys). ``rows``: None for every row, or the row indices to compute."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Sq, _ = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if k_end is None:
+        k_end = Skv
+    group = Hq // Hkv
+    rows = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = rows.shape[0]
+    j = np.arange(Skv)
+    o = np.zeros((B, Hq, R, v.shape[3]))
+    lse = np.full((B, Hq, R), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            for c0 in range(0, R, row_chunk):
+                idx = rows[c0:c0 + row_chunk]
+                visible = (j[None, :] >= k_begin) & (j[None, :] < k_end) & (j[None, :] <= q_offset + idx[:, None])
+                seen = visible.any(axis=1)
+                if not seen.any():
+                    continue
+                s = scale * (q[b, h, idx[seen]] @ k[b, g].T)
+                s = np.where(visible[seen], s, -np.inf)
+                m = s.max(axis=1)
+                w = np.exp(s - m[:, None])
+                l = w.sum(axis=1)
+                out = np.flatnonzero(seen) + c0
+                o[b, h, out] = (w @ v[b, g]) / l[:, None]
+                lse[b, h, out] = m + np.log(l)
+    return o, lse
+
+
+def merge_partials(o_parts, lse_parts):
+    """Combine partial attention results over disjoint key sets, in float64.
+
+    Zyphra "Inference Wave 2", section on CSA dual-scope decode: partial outputs and their
+    log-sum-exp statistics merge into the result of one pass over all keys. With parts p
+    of one row: M = max_p LSE_p, w_p = exp(LSE_p - M), O = sum_p w_p O_p / sum_p w_p,
+    LSE = M + ln sum_p w_p. A part with LSE_p = -inf holds no key of the row and has weight
+    zero; a row that no part saw gets O = 0, LSE = -inf.
+
+    o_parts: [P, ..., Dv]; lse_parts: [P, ...]. Returns (o [..., Dv], lse [...])."""
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    m = lse_parts.max(axis=0)
+    seen = m > -np.inf
+    w = np.where(seen[None], np.exp(lse_parts - np.where(seen, m, 0.0)[None]), 0.0)
+    wsum = w.sum(axis=0)
+    o = np.zeros(o_parts.shape[1:])
+    o[seen] = (np.einsum("p...,p...d->...d", w, o_parts)[seen]) / wsum[seen][:, None]
+    lse = np.where(seen, m + np.log(np.where(seen, wsum, 1.0)), -np.inf)
+    return o, lse
