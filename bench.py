@@ -12,7 +12,8 @@ inputs. FLOPs follow the FlashAttention causal convention, 2 (Dqk + Dv) S^2 / 2 
 Prints one JSON line. ``value`` is FP8 whole-step throughput; the attention kernel
 alone is timed with HIP events on the stream it runs on and reported against the
 datasheet dense FP8 peak in ``roofline``; the opt-in lean-probability FP8 mode is
-reported in ``fp8_lean`` and BF16 in ``bf16``. The CPU baseline times the fp64 oracle
+reported in ``fp8_lean`` and BF16 in ``bf16``; ``range`` times the range entry points
+(chunked prefill, split-KV with the merge kernel and its HBM roofline). The CPU baseline times the fp64 oracle
 on a bounded sample (whole query heads, about 15 s) on the host cores; the heads it
 computed also give a full-size parity figure (``sampled_rel_l2_fp8``).
 
@@ -227,6 +228,48 @@ def sustained(tel, fn, flops, peak, settle_s, window_s, stream, torch):
     return rec
 
 
+def range_paths(w, qc, kc, vc, qs, ks, vs, steps, warmup, stream, torch, zy):
+    """The range entry points at the benchmark shape (FP8, exact probabilities): the second
+    half of the sequence as one chunk of query rows against its causal prefix (chunked
+    prefill), and the keys split into two windows whose partial results zyfa_attn_merge
+    combines (split-KV). Times from HIP events on the launch stream."""
+    S, blk, tau = w.S, w.scale_block, w.softmax_scale
+    half = (S // 2) // blk * blk
+    dev = qc.device
+    per_row_flops = 2.0 * (w.Dqk + w.Dv) * w.B * w.Hq
+    # chunk: rows half .. S-1, each row i sees i + 1 keys (S^2/2 convention: (S^2 - half^2) / 2)
+    qc2, qs2 = qc[:, :, half:].contiguous(), qs[:, :, half // blk:].contiguous()
+    oc = torch.empty((w.B, w.Hq, S - half, w.Dv), dtype=torch.bfloat16, device=dev)
+    ms, _ = time_kernel(lambda: zy.attn_fwd_fp8_range(qc2, kc, vc, qs2, ks, vs, blk, half, 0, S, tau, o=oc),
+                        steps, warmup, stream, torch)
+    chunk_flops = per_row_flops * (S * S - half * half) / 2
+    rec = {"chunk": {"q_offset": half, "rows": S - half, "keys": S, "ms": ms, "tflops": chunk_flops / ms / 1e9,
+                     "frac_of_fp8_peak": chunk_flops / ms / 1e9 / PEAK_FP8}}
+    # split-KV: windows [0, half) and [half, S) over all rows, then the merge
+    o_parts = torch.empty((2, w.B, w.Hq, S, w.Dv), dtype=torch.bfloat16, device=dev)
+    l_parts = torch.empty((2, w.B, w.Hq, S), dtype=torch.float32, device=dev)
+    om = torch.empty((w.B, w.Hq, S, w.Dv), dtype=torch.bfloat16, device=dev)
+    lm = torch.empty((w.B, w.Hq, S), dtype=torch.float32, device=dev)
+    part_ms = []
+    for i, (lo, hi) in enumerate(((0, half), (half, S))):
+        ms, _ = time_kernel(lambda: zy.attn_fwd_fp8_range(qc, kc, vc, qs, ks, vs, blk, 0, lo, hi, tau, o=o_parts[i],
+                                                          lse=l_parts[i]), steps, warmup, stream, torch)
+        part_ms.append(ms)
+    merge_ms, _ = time_kernel(lambda: zy.attn_merge(o_parts, l_parts, o=om, lse=lm), steps, warmup, stream, torch)
+    rows = w.B * w.Hq * S
+    merge_bytes = 3 * rows * (2 * w.Dv + 4)  # read two parts (O and LSE), write one
+    rec["split_kv"] = {"windows": [[0, half], [half, S]], "parts_ms": part_ms, "merge_ms": merge_ms,
+                       "total_ms": sum(part_ms) + merge_ms,
+                       "tflops": w.flops / (sum(part_ms) + merge_ms) / 1e9,
+                       "merge_roofline": {"bound": "hbm", "achieved": merge_bytes / merge_ms / 1e6, "peak": PEAK_HBM_GBS,
+                                          "unit": "GB/s", "frac": merge_bytes / merge_ms / 1e6 / PEAK_HBM_GBS,
+                                          "bytes_per_launch": merge_bytes}}
+    print(f"[bench] range: chunk {rec['chunk']['ms']:.3f} ms, split-KV parts {part_ms[0]:.3f} + {part_ms[1]:.3f} ms, "
+          f"merge {merge_ms:.3f} ms ({merge_bytes / merge_ms / 1e6:.0f} GB/s)", file=sys.stderr, flush=True)
+    del o_parts, l_parts, om, lm, oc, qc2
+    return rec
+
+
 def other_workloads(names, steps, warmup, torch, zy):
     """Kernel throughput on the other benchmark shapes (4K MHA, 32K MLA, 16K activation-like
     with and without the Hadamard rotation of Q and K): FP8 exact and lean, and BF16.
@@ -277,6 +320,7 @@ def main():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-lean", action="store_true", help="skip the lean-probability FP8 mode")
     ap.add_argument("--no-others", action="store_true", help="skip the other workload shapes")
+    ap.add_argument("--no-range", action="store_true", help="skip the chunked-prefill and split-KV measurements")
     ap.add_argument("--sustain", type=float, default=4.0,
                     help="seconds of back-to-back launches per headline kernel, after 1.5 s of settling, "
                          "with clock and power telemetry (0: skip)")
@@ -456,6 +500,10 @@ def main():
         "bf16": bf16,
         "sustained": sustained_rec,
     }
+
+    if not args.no_range:
+        line["range"] = range_paths(w, qc, kc, vc, qs, ks, vs, max(args.steps // 5, 5), max(args.warmup // 10, 5), stream,
+                                    torch, zy)
 
     if not args.no_others:
         others = [n for n in ("mha4k", "mla32k", "act16k") if n != w.name]

@@ -12,6 +12,11 @@ Functions mirror the C entry points:
 * ``attn_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, scale_block, softmax_scale)``
   -> (o bfloat16, lse float32 or None)
 * ``attn_fwd_bf16(q, k, v, softmax_scale)`` -> (o bfloat16, lse float32 or None)
+* ``attn_fwd_fp8_range(..., q_offset, k_begin, k_end)`` / ``attn_fwd_bf16_range``: a chunk
+  of query rows (row i at sequence position q_offset + i) against the key window
+  [k_begin, k_end) -> (o, lse or None)
+* ``attn_merge(o_parts, lse_parts)`` -> (o bfloat16, lse float32 or None): combine partial
+  results over disjoint key sets
 """
 
 import math
@@ -21,7 +26,8 @@ import torch
 from . import _lib
 from ._lib import ZyfaError, load
 
-__all__ = ["quantize_fp8", "attn_fwd_fp8", "attn_fwd_bf16", "ZyfaError", "load", "abi_version"]
+__all__ = ["quantize_fp8", "attn_fwd_fp8", "attn_fwd_bf16", "attn_fwd_fp8_range", "attn_fwd_bf16_range", "attn_merge",
+           "ZyfaError", "load", "abi_version"]
 
 
 def abi_version() -> int:
@@ -130,4 +136,90 @@ def attn_fwd_bf16(q, k, v, softmax_scale=None, o=None, lse=None, return_lse: boo
     o, po, lse, plse = _outputs(q, B, Hq, S, Dv, o, lse, return_lse)
     st = load().zyfa_attn_fwd_bf16(pq, pk, pv, po, plse, B, Hq, Hkv, S, Dqk, Dv, float(softmax_scale), _stream())
     _lib.check(st, "zyfa_attn_fwd_bf16")
+    return o, lse
+
+
+def _range_shapes(q, k, v):
+    B, Hq, Sq, Dqk = q.shape
+    Bk, Hkv, Skv, Dk = k.shape
+    if (Bk, Dk) != (B, Dqk) or tuple(v.shape[:3]) != (B, Hkv, Skv):
+        raise ValueError(f"inconsistent shapes q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    return B, Hq, Hkv, Sq, Skv, Dqk, v.shape[3]
+
+
+def attn_fwd_fp8_range(q, k, v, q_scale, k_scale, v_scale, scale_block: int, q_offset: int = 0, k_begin: int = 0,
+                       k_end=None, softmax_scale=None, o=None, lse=None, return_lse: bool = False,
+                       lean: bool = False):
+    """Causal attention of the query rows q [B, Hq, Sq, Dqk] (row i at sequence position
+    q_offset + i) against the keys [k_begin, k_end) of k, v [B, Hkv, Skv, D] (e4m3 codes,
+    uint8), with float32 block scales q_scale [B, Hq, ceil(Sq / blk)] and k_scale, v_scale
+    [B, Hkv, ceil(Skv / blk)]. k_end defaults to Skv. Rows that see no key get O = 0 and
+    LSE = -inf. Returns (o bfloat16 [B, Hq, Sq, Dv], lse or None)."""
+    pq = _dev(q, "q", torch.uint8, 4)
+    pk = _dev(k, "k", torch.uint8, 4)
+    pv = _dev(v, "v", torch.uint8, 4)
+    B, Hq, Hkv, Sq, Skv, Dqk, Dv = _range_shapes(q, k, v)
+    nbq = (Sq + scale_block - 1) // scale_block if scale_block > 0 else 0
+    nbk = (Skv + scale_block - 1) // scale_block if scale_block > 0 else 0
+    psq = _dev(q_scale, "q_scale", torch.float32, 3)
+    psk = _dev(k_scale, "k_scale", torch.float32, 3)
+    psv = _dev(v_scale, "v_scale", torch.float32, 3)
+    if (tuple(q_scale.shape) != (B, Hq, nbq) or tuple(k_scale.shape) != (B, Hkv, nbk)
+            or tuple(v_scale.shape) != (B, Hkv, nbk)):
+        raise ValueError("scale tensors have the wrong shape")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(Dqk)
+    if k_end is None:
+        k_end = Skv
+    o, po, lse, plse = _outputs(q, B, Hq, Sq, Dv, o, lse, return_lse)
+    st = load().zyfa_attn_fwd_fp8_range(pq, pk, pv, psq, psk, psv, scale_block, po, plse, B, Hq, Hkv, Sq, Skv,
+                                        int(q_offset), int(k_begin), int(k_end), Dqk, Dv, float(softmax_scale),
+                                        int(bool(lean)), _stream())
+    _lib.check(st, "zyfa_attn_fwd_fp8_range")
+    return o, lse
+
+
+def attn_fwd_bf16_range(q, k, v, q_offset: int = 0, k_begin: int = 0, k_end=None, softmax_scale=None, o=None,
+                        lse=None, return_lse: bool = False):
+    """attn_fwd_fp8_range on bfloat16 tensors. Returns (o bfloat16 [B, Hq, Sq, Dv], lse or None)."""
+    pq = _dev(q, "q", torch.bfloat16, 4)
+    pk = _dev(k, "k", torch.bfloat16, 4)
+    pv = _dev(v, "v", torch.bfloat16, 4)
+    B, Hq, Hkv, Sq, Skv, Dqk, Dv = _range_shapes(q, k, v)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(Dqk)
+    if k_end is None:
+        k_end = Skv
+    o, po, lse, plse = _outputs(q, B, Hq, Sq, Dv, o, lse, return_lse)
+    st = load().zyfa_attn_fwd_bf16_range(pq, pk, pv, po, plse, B, Hq, Hkv, Sq, Skv, int(q_offset), int(k_begin),
+                                         int(k_end), Dqk, Dv, float(softmax_scale), _stream())
+    _lib.check(st, "zyfa_attn_fwd_bf16_range")
+    return o, lse
+
+
+def attn_merge(o_parts, lse_parts, o=None, lse=None, return_lse: bool = False):
+    """Combine partial results over disjoint key sets: o_parts [P, ..., Dv] bfloat16 and
+    lse_parts [P, ...] float32 (natural log; -inf where a part saw no key of the row).
+    Returns (o bfloat16 [..., Dv], lse float32 [...] or None)."""
+    if o_parts.dim() < 2 or tuple(lse_parts.shape) != tuple(o_parts.shape[:-1]):
+        raise ValueError(f"inconsistent shapes o_parts {tuple(o_parts.shape)} lse_parts {tuple(lse_parts.shape)}")
+    po_p = _dev(o_parts, "o_parts", torch.bfloat16, o_parts.dim())
+    pl_p = _dev(lse_parts, "lse_parts", torch.float32, lse_parts.dim())
+    P, Dv = o_parts.shape[0], o_parts.shape[-1]
+    rows = lse_parts.numel() // P
+    out_shape = tuple(o_parts.shape[1:])
+    if o is None:
+        o = torch.empty(out_shape, dtype=torch.bfloat16, device=o_parts.device)
+    po = _dev(o, "o", torch.bfloat16, len(out_shape))
+    if tuple(o.shape) != out_shape:
+        raise ValueError("o has the wrong shape")
+    if lse is None and return_lse:
+        lse = torch.empty(out_shape[:-1], dtype=torch.float32, device=o_parts.device)
+    plse = None
+    if lse is not None:
+        plse = _dev(lse, "lse", torch.float32, len(out_shape) - 1)
+        if tuple(lse.shape) != out_shape[:-1]:
+            raise ValueError("lse has the wrong shape")
+    st = load().zyfa_attn_merge(po_p, pl_p, P, po, plse, rows, Dv, _stream())
+    _lib.check(st, "zyfa_attn_merge")
     return o, lse

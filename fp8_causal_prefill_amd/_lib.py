@@ -25,6 +25,9 @@ _SIGNATURES = {
     "zyfa_attn_fwd_fp8": ([_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp], _i),
     "zyfa_attn_fwd_fp8_lean": ([_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp], _i),
     "zyfa_attn_fwd_bf16": ([_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp], _i),
+    "zyfa_attn_fwd_fp8_range": ([_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp] + [_i] * 10 + [_f, _i, _vp], _i),
+    "zyfa_attn_fwd_bf16_range": ([_vp, _vp, _vp, _vp, _vp] + [_i] * 10 + [_f, _vp], _i),
+    "zyfa_attn_merge": ([_vp, _vp, _i, _vp, _vp, ctypes.c_longlong, _i, _vp], _i),
 }
 
 

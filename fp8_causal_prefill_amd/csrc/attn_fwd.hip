@@ -58,6 +58,9 @@
 namespace zyfa {
 
 constexpr float kLazyThreshold = 8.0f;
+// Exponent reference of a row that has seen no key yet: finite, so that masked scores give
+// probabilities of exactly zero, and far below any score, so the first visible key moves it.
+constexpr float kRefEmpty = -1e30f;
 // Lean probabilities: code = round(8 y + kLeanBias) for p = 2^y. 56 is the code of 1.0;
 // the linear code overestimates 2^y inside each binade by 0 to 0.69 codes (mean 0.46),
 // and subtracting that mean minimises the error of the normalised output.
@@ -102,6 +105,9 @@ struct Cfg {
   static_assert(BM % (2 * BN) == 0, "steady iterations rely on an even number of key tiles per query tile");
 };
 
+// Key positions inside the kernel are relative to the window's first key k_begin: the
+// window holds keys 0 .. Sk - 1, and query row i (of the Q tensor) sits at position
+// d + i, so it sees keys j <= min(d + i, Sk - 1). A row with d + i < 0 sees no key.
 struct AttnParams {
   const char* q;
   const char* k;
@@ -111,7 +117,13 @@ struct AttnParams {
   const float* v_scale;
   uint16_t* o;
   float* lse;
-  int B, Hq, Hkv, S, nb, scale_shift, n_qtiles;  // scale block = 1 << scale_shift tokens
+  int B, Hq, Hkv;
+  int Sq;       // rows per head of Q, O and LSE
+  int Skv;      // rows per head of K and V
+  int k_begin;  // first key of the window (a multiple of the key tile)
+  int Sk;       // keys in the window
+  int d;        // position of query row 0 relative to k_begin
+  int nbq, nbk, scale_shift, n_qtiles;  // scale blocks of Q and of K/V (1 << scale_shift tokens)
   float scale_log2;  // softmax_scale * log2(e)
 };
 
@@ -136,7 +148,8 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   const int wave = tid >> 6;
   const int h = lane >> 5;
   const int l32 = lane & 31;
-  const int S = p.S;
+  const int Sq = p.Sq;
+  const int Sk = p.Sk;
 
   // ---- work item: (batch, query head, query tile), heaviest tile first ----
   const int NH = p.B * p.Hq;
@@ -151,22 +164,43 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   const int hkv = hq / (p.Hq / p.Hkv);
 
   const int q0_wg = qt * C::BM;
-  const int q0 = q0_wg + wave * 32;
-  // every wave runs the workgroup's trip count; tiles past a wave's rows are fully masked
-  const int n = (min(q0_wg + C::BM, S) - 1) / C::BN + 1;
-  const int my_q = q0 + l32;
+  const int q0 = q0_wg + __builtin_amdgcn_readfirstlane(wave) * 32;  // (wave-uniform)
+  // this lane's query row, recomputed from the lane id where needed (not kept in a register)
+  auto row_of_lane = [&] { return q0 + (int)(__lane_id() & 31); };
+  const int my_q = row_of_lane();
+  // last key of the window visible to this lane's row, and to the wave's first row
+  const int lim_q = min(p.d + my_q, Sk - 1);
+  const int lim_w = min(p.d + q0, Sk - 1);
+  // every wave runs the workgroup's trip count (key tiles up to the last one its last row
+  // sees); tiles past a wave's rows are fully masked
+  const int last_key = min(p.d + min(q0_wg + C::BM, Sq) - 1, Sk - 1);
+  const int n = last_key < 0 ? 0 : last_key / C::BN + 1;
 
   const size_t bh_q = (size_t)(b * p.Hq + hq);
   const size_t bh_kv = (size_t)(b * p.Hkv + hkv);
-  const char* kbase = p.k + bh_kv * S * C::KROW;
-  const char* vbase = p.v + bh_kv * S * C::VROW;
-  const float* kscale = p.k_scale + bh_kv * p.nb;
-  const float* vscale = p.v_scale + bh_kv * p.nb;
+
+  if (n == 0) {
+    // no row of the workgroup sees a key of the window: O = 0, LSE = -inf
+    if (my_q < Sq) {
+      uint16_t* orow = p.o + (bh_q * Sq + my_q) * C::DV;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) *(uint2*)(orow + 32 * d + 8 * r4 + 4 * h) = uint2{0u, 0u};
+      if (p.lse != nullptr && h == 0) p.lse[bh_q * Sq + my_q] = -INFINITY;
+    }
+    return;
+  }
+
+  const char* kbase = p.k + (bh_kv * p.Skv + p.k_begin) * C::KROW;
+  const char* vbase = p.v + (bh_kv * p.Skv + p.k_begin) * C::VROW;
+  const float* kscale = p.k_scale + bh_kv * p.nbk;
+  const float* vscale = p.v_scale + bh_kv * p.nbk;
 
   // ---- Q operand (B of S^T = K Q^T): lane holds Q[my_q][c*KSTEP + h*KSTEP/2 ...] ----
   QOp<FP8> qreg[C::NKS];
   {
-    const char* qrow = p.q + (bh_q * S + min(my_q, S - 1)) * C::KROW;
+    const char* qrow = p.q + (bh_q * Sq + min(my_q, Sq - 1)) * C::KROW;
 #pragma unroll
     for (int c = 0; c < C::NKS; ++c) {
       const char* src = qrow + (c * C::KSTEP + h * (C::KSTEP / 2)) * C::ESZ;
@@ -180,14 +214,14 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     }
   }
   float c_q = p.scale_log2;  // multiplies raw scores into base-2 units (times the tile's k scale for FP8)
-  if constexpr (FP8) c_q *= p.q_scale[bh_q * p.nb + (min(q0, S - 1) >> p.scale_shift)];
+  if constexpr (FP8) c_q *= p.q_scale[bh_q * p.nbq + (min(q0, Sq - 1) >> p.scale_shift)];
 
   // ---- direct global -> LDS staging ----
   // 16-byte position pos of a buffer is (column block, row r, stored chunk); the lane
   // that fills it fetches the global chunk stored there. Each wave instruction fills 64
   // consecutive positions (1 KiB), lane l at position base + l. A lane's source offset
-  // within a tile does not depend on the tile; only the last tile of a sequence whose
-  // length is not a multiple of BN clamps its rows to S - 1.
+  // within a tile does not depend on the tile; only the last tile of a window whose
+  // length is not a multiple of BN clamps its rows to the window's last key.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // does this wave copy chunk i of a tile (always, unless the tile's last round of
   // copies does not reach every wave)?
@@ -218,7 +252,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   auto fill_k = [&](int t, int buf) {
     const int t0 = t * C::BN;
     const uint32_t dst = k_lds + buf * C::KBUF + wave_u * 64 * 16;
-    if (t0 + C::BN <= S) {
+    if (t0 + C::BN <= Sk) {
       const char* tile = kbase + (size_t)t0 * C::KROW;
 #pragma unroll
       for (int i = 0; i < C::KCHUNKS; ++i)
@@ -226,7 +260,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     } else {
 #pragma unroll
       for (int i = 0; i < C::KCHUNKS; ++i) {
-        const int gr = min(t0 + k_pos_row(i), S - 1);
+        const int gr = min(t0 + k_pos_row(i), Sk - 1);
         if (k_live(i)) lds_copy16(kbase + (size_t)gr * C::KROW + k_pos_off(i), dst + i * C::THREADS * 16);
       }
     }
@@ -234,7 +268,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   auto fill_v = [&](int t, int buf) {
     const int t0 = t * C::BN;
     const uint32_t dst = v_lds + buf * C::VBUF + wave_u * 64 * 16;
-    if (t0 + C::BN <= S) {
+    if (t0 + C::BN <= Sk) {
       const char* tile = vbase + (size_t)t0 * C::VROW;
 #pragma unroll
       for (int i = 0; i < C::VCHUNKS; ++i)
@@ -242,7 +276,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     } else {
 #pragma unroll
       for (int i = 0; i < C::VCHUNKS; ++i) {
-        const int gr = min(t0 + v_pos_row(i), S - 1);
+        const int gr = min(t0 + v_pos_row(i), Sk - 1);
         if (v_live(i)) lds_copy16(vbase + (size_t)gr * C::VROW + v_pos_off(i), dst + i * C::THREADS * 16);
       }
     }
@@ -310,18 +344,18 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   };
   auto mask = [&](v16f (&s)[2], int t) {
     const int kt = t * C::BN;
-    if (kt + C::BN - 1 > q0) {
+    if (kt + C::BN - 1 > lim_w) {
 #pragma unroll
       for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (kt + 32 * g + 8 * (r >> 2) + 4 * h + (r & 3) > my_q) s[g][r] = -INFINITY;
+          if (kt + 32 * g + 8 * (r >> 2) + 4 * h + (r & 3) > lim_q) s[g][r] = -INFINITY;
     }
   };
   // the same mask, branch-free (one compare and one select per score): for steady
   // iterations over the diagonal tiles, where a branch would split the slot schedule
   auto mask_nb = [&](v16f (&s)[2], int t) {
-    const int lim = my_q - t * C::BN - 4 * h;  // key offsets within the tile up to lim stay
+    const int lim = lim_q - t * C::BN - 4 * h;  // key offsets within the tile up to lim stay
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -353,12 +387,13 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   wait_fills();
   __syncthreads();
 
+  // key tiles that every row of the workgroup sees whole (full tiles inside the window)
+  const int n_full = max(0, (min(p.d + q0_wg, Sk - 1) + 1) / C::BN);
   // iterations t < n_steady need no causal mask on tile t+1 in any wave and prefetch
-  // K_{t+2}: their bodies are branch-free and carry a fixed instruction schedule. With
-  // BM a multiple of 2 BN, (q0_wg + 1) / BN - 1 is odd, so the even n_steady is at most
-  // q0_wg / BN - 2 and every tile they fetch (t + 2 <= q0_wg / BN - 1) ends before row
-  // q0_wg < S: no clamping.
-  const int n_steady = max(0, min(n - 2, (q0_wg + 1) / C::BN - 1)) & ~1;
+  // K_{t+2}: their bodies are branch-free and carry a fixed instruction schedule. The even
+  // n_steady is at most n_full - 2, so every tile they fetch (t + 2 <= n_full - 1) is a
+  // full tile inside the window: no clamping.
+  const int n_steady = max(0, min(n - 2, n_full - 2)) & ~1;
 
   v16f sa[2], sb[2];
   qk(0, sa);
@@ -366,16 +401,18 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   __syncthreads();
   mask(sa, 0);
   float c_cur = c_q;
-  if constexpr (FP8) c_cur *= kscale[0];
-  float xmax0 = rowmax(sa) * c_cur;  // tile 0 always holds key 0 <= every row: finite
-  float m_ref = ceilf(xmax0);
+  if constexpr (FP8) c_cur *= kscale[min(p.k_begin >> p.scale_shift, p.nbk - 1)];
+  // tile 0 holds the window's key 0, which every row at a position >= 0 sees: finite there
+  float xmax0 = rowmax(sa) * c_cur;
+  float m_ref = xmax0 > -INFINITY ? ceilf(xmax0) : kRefEmpty;
   bool rescale = false;
 
   // epilogue: O / l as bfloat16, and the log-sum-exp
   auto store_out = [&](float l_sum) {
-    if (q0 >= S || my_q >= S) return;
-    const float inv_l = 1.0f / l_sum;
-    uint16_t* orow = p.o + (bh_q * S + my_q) * C::DV;
+    const int my_q = row_of_lane();
+    if (q0 >= Sq || my_q >= Sq) return;
+    const float inv_l = l_sum > 0.0f ? 1.0f / l_sum : 0.0f;  // a row with no key: O = 0, LSE = -inf
+    uint16_t* orow = p.o + (bh_q * Sq + my_q) * C::DV;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -385,7 +422,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
         w.y = pack_bf16x2(oacc[d][4 * r4 + 2] * inv_l, oacc[d][4 * r4 + 3] * inv_l);
         *(uint2*)(orow + 32 * d + 8 * r4 + 4 * h) = w;
       }
-    if (p.lse != nullptr && h == 0) p.lse[bh_q * S + my_q] = kLn2 * (m_ref + log2f(l_sum));
+    if (p.lse != nullptr && h == 0) p.lse[bh_q * Sq + my_q] = kLn2 * (m_ref + log2f(l_sum));
   };
 
   if constexpr (FP8) {
@@ -407,14 +444,14 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     };
     // K and V scales of tile t+1 while iteration t runs; the loads for tile t+2 are
     // issued at the top of iteration t, ahead of the tile fills whose wait covers them
-    auto sidx = [&](int tile) { return min((tile * C::BN) >> p.scale_shift, p.nb - 1); };
+    auto sidx = [&](int tile) { return min((p.k_begin + tile * C::BN) >> p.scale_shift, p.nbk - 1); };
     float ks_next = kscale[sidx(1)];
     float vs_next = vscale[sidx(1)];
     auto block_exp = [&](float xmax) { return (int)fmaxf(floorf(xmax - m_ref), -126.0f); };
 
     float rv_cur;
     int sv_cur;
-    vsplit(vscale[0], rv_cur, sv_cur);
+    vsplit(vscale[sidx(0)], rv_cur, sv_cur);
     int eb_cur = block_exp(xmax0);
 
     v8i pa = v8i{0}, pb = v8i{0};
@@ -466,7 +503,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
         float a = 1.0f;
         if (rescale) {
           const float m_new = grow ? ceilf(xmax_pend) : m_ref;
-          la = (int)(m_ref - m_new);
+          la = (int)fmaxf(m_ref - m_new, -256.0f);  // (from an empty row's reference: any factor below 2^-149 is 0)
           a = fast_exp2((float)la);
           m_ref = m_new;
           eb_cur = block_exp(xmax_pend);
@@ -784,8 +821,8 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     constexpr int MX0_SLOT = 16 + C::NKS + 1;
     static_assert(C::NKS == 8 || C::NKS == 12, "BF16 slot plan");
     // steady iterations: tile t unmasked in every row of the workgroup, K_{t+2} a full
-    // tile within S, and a next tile
-    const int n_steady_b = max(0, min(q0_wg / C::BN, min(S / C::BN - 2, n - 1)));
+    // tile inside the window, and a next tile
+    const int n_steady_b = max(0, min(n_full, min(Sk / C::BN - 2, n - 1)));
     float mx0 = -INFINITY;  // row maxima of the current tile's key group 0 (this lane's half)
     // MASKED: the same schedule over the diagonal tiles (any iteration with a next tile):
     // tile t's scores are masked in slot 0 and its maxima taken over both key groups
@@ -910,10 +947,15 @@ static hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   p.B = a.B;
   p.Hq = a.Hq;
   p.Hkv = a.Hkv;
-  p.S = a.S;
+  p.Sq = a.Sq;
+  p.Skv = a.Skv;
+  p.k_begin = a.k_begin;
+  p.Sk = a.k_end - a.k_begin;
+  p.d = a.q_offset - a.k_begin;
   p.scale_shift = FP8 ? (a.scale_block == 64 ? 6 : 7) : 0;
-  p.nb = FP8 ? (a.S + a.scale_block - 1) / a.scale_block : 0;
-  p.n_qtiles = (a.S + C::BM - 1) / C::BM;
+  p.nbq = FP8 ? (a.Sq + a.scale_block - 1) / a.scale_block : 0;
+  p.nbk = FP8 ? (a.Skv + a.scale_block - 1) / a.scale_block : 0;
+  p.n_qtiles = (a.Sq + C::BM - 1) / C::BM;
   p.scale_log2 = a.softmax_scale * kLog2e;
   const long long grid = (long long)p.n_qtiles * a.B * a.Hq;
   hipLaunchKernelGGL((attn_fwd_kernel<FP8, DQK, LEAN>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);

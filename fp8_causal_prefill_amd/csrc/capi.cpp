@@ -31,23 +31,35 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // Largest element count any tensor may have (keeps every 64-bit offset far from overflow
 // and every per-head row count within int range).
 constexpr long long kMaxElems = 1LL << 40;
+// Largest sequence position a query row may have (keeps position arithmetic in int range).
+constexpr long long kMaxPosition = 1LL << 30;
 
 zyfa_status check_attn_common(const void* q, const void* k, const void* v, const void* o, const void* lse, int B,
-                              int Hq, int Hkv, int S, int Dqk, int Dv, float softmax_scale) {
+                              int Hq, int Hkv, int Sq, int Skv, int q_offset, int k_begin, int k_end, int Dqk, int Dv,
+                              float softmax_scale) {
   if (!q || !k || !v || !o) return fail(ZYFA_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-null");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
     return fail(ZYFA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0)
-    return fail(ZYFA_ERR_INVALID_ARGUMENT, "B, Hq, Hkv and S must be positive (got %d, %d, %d, %d)", B, Hq, Hkv, S);
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "B, Hq, Hkv and the sequence lengths must be positive (got %d, %d, %d, %d, %d)",
+                B, Hq, Hkv, Sq, Skv);
   if (Hq % Hkv != 0) return fail(ZYFA_ERR_INVALID_ARGUMENT, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale))
     return fail(ZYFA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and positive");
   if (Dqk <= 0 || Dv <= 0) return fail(ZYFA_ERR_INVALID_ARGUMENT, "head dims must be positive");
-  if ((long long)B * Hq * S * (Dqk > Dv ? Dqk : Dv) > kMaxElems)
+  if (q_offset < 0 || (long long)q_offset + Sq > kMaxPosition)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "q_offset (%d) must be >= 0 and q_offset + Sq at most 2^30", q_offset);
+  if (k_begin < 0 || k_begin >= k_end || k_end > Skv)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "the key window [%d, %d) must be non-empty and inside [0, Skv = %d)",
+                k_begin, k_end, Skv);
+  if (k_begin % zyfa::kKeyTile != 0)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "k_begin (%d) must be a multiple of %d", k_begin, zyfa::kKeyTile);
+  const long long dmax = Dqk > Dv ? Dqk : Dv;
+  if ((long long)B * Hq * Sq * dmax > kMaxElems || (long long)B * Hkv * Skv * dmax > kMaxElems)
     return fail(ZYFA_ERR_INVALID_ARGUMENT, "tensor too large");
   if (!((Dqk == 128 && Dv == 128) || (Dqk == 192 && Dv == 128)))
     return fail(ZYFA_ERR_UNSUPPORTED, "(Dqk, Dv) = (%d, %d) is not supported; use (128, 128) or (192, 128)", Dqk, Dv);
-  const long long n_qtiles = (S + 127) / 128;
+  const long long n_qtiles = (Sq + 127) / 128;
   if (n_qtiles * B * Hq > 0x7FFFFFFFLL) return fail(ZYFA_ERR_UNSUPPORTED, "grid too large");
   if ((o == q || o == k || o == v) || (lse && (lse == q || lse == k || lse == v || lse == o)))
     return fail(ZYFA_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
@@ -99,9 +111,10 @@ zyfa_status zyfa_quantize_fp8(const void* x, int x_is_bf16, uint8_t* codes, floa
 
 static zyfa_status attn_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_scale,
                             const float* k_scale, const float* v_scale, int scale_block, uint16_t* o, float* lse,
-                            int B, int Hq, int Hkv, int S, int Dqk, int Dv, float softmax_scale, void* stream,
-                            bool lean) {
-  zyfa_status st = check_attn_common(q, k, v, o, lse, B, Hq, Hkv, S, Dqk, Dv, softmax_scale);
+                            int B, int Hq, int Hkv, int Sq, int Skv, int q_offset, int k_begin, int k_end, int Dqk,
+                            int Dv, float softmax_scale, void* stream, bool lean) {
+  zyfa_status st = check_attn_common(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, q_offset, k_begin, k_end, Dqk, Dv,
+                                     softmax_scale);
   if (st != ZYFA_OK) return st;
   if (!q_scale || !k_scale || !v_scale) return fail(ZYFA_ERR_INVALID_ARGUMENT, "scale pointers must be non-null");
   if (!aligned16(q_scale) || !aligned16(k_scale) || !aligned16(v_scale))
@@ -109,8 +122,22 @@ static zyfa_status attn_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v
   if (scale_block != 64 && scale_block != 128)
     return fail(ZYFA_ERR_INVALID_ARGUMENT, "scale_block must be 64 or 128 (got %d)", scale_block);
 
-  zyfa::AttnArgs a{q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, S, Dqk, Dv, scale_block, softmax_scale};
+  zyfa::AttnArgs a{q,   k,        v,       q_scale, k_scale, v_scale, o,           lse,          B, Hq, Hkv,
+                   Sq,  Skv,      q_offset, k_begin, k_end,  Dqk,     Dv,          scale_block, softmax_scale};
   hipError_t e = zyfa::launch_attn_fwd_fp8(a, lean, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ZYFA_ERR_LAUNCH, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+static zyfa_status attn_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse, int B,
+                             int Hq, int Hkv, int Sq, int Skv, int q_offset, int k_begin, int k_end, int Dqk, int Dv,
+                             float softmax_scale, void* stream) {
+  zyfa_status st = check_attn_common(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, q_offset, k_begin, k_end, Dqk, Dv,
+                                     softmax_scale);
+  if (st != ZYFA_OK) return st;
+  zyfa::AttnArgs a{q,   k,        v,       nullptr, nullptr, nullptr, o,  lse, B, Hq, Hkv,
+                   Sq,  Skv,      q_offset, k_begin, k_end,  Dqk,     Dv, 0,   softmax_scale};
+  hipError_t e = zyfa::launch_attn_fwd_bf16(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(ZYFA_ERR_LAUNCH, "attention launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -118,25 +145,55 @@ static zyfa_status attn_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v
 zyfa_status zyfa_attn_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_scale,
                               const float* k_scale, const float* v_scale, int scale_block, uint16_t* o, float* lse,
                               int B, int Hq, int Hkv, int S, int Dqk, int Dv, float softmax_scale, void* stream) {
-  return attn_fp8(q, k, v, q_scale, k_scale, v_scale, scale_block, o, lse, B, Hq, Hkv, S, Dqk, Dv, softmax_scale,
-                  stream, false);
+  return attn_fp8(q, k, v, q_scale, k_scale, v_scale, scale_block, o, lse, B, Hq, Hkv, S, S, 0, 0, S, Dqk, Dv,
+                  softmax_scale, stream, false);
 }
 
 zyfa_status zyfa_attn_fwd_fp8_lean(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_scale,
                                    const float* k_scale, const float* v_scale, int scale_block, uint16_t* o,
                                    float* lse, int B, int Hq, int Hkv, int S, int Dqk, int Dv, float softmax_scale,
                                    void* stream) {
-  return attn_fp8(q, k, v, q_scale, k_scale, v_scale, scale_block, o, lse, B, Hq, Hkv, S, Dqk, Dv, softmax_scale,
-                  stream, true);
+  return attn_fp8(q, k, v, q_scale, k_scale, v_scale, scale_block, o, lse, B, Hq, Hkv, S, S, 0, 0, S, Dqk, Dv,
+                  softmax_scale, stream, true);
 }
 
 zyfa_status zyfa_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
                                int B, int Hq, int Hkv, int S, int Dqk, int Dv, float softmax_scale, void* stream) {
-  zyfa_status st = check_attn_common(q, k, v, o, lse, B, Hq, Hkv, S, Dqk, Dv, softmax_scale);
-  if (st != ZYFA_OK) return st;
-  zyfa::AttnArgs a{q, k, v, nullptr, nullptr, nullptr, o, lse, B, Hq, Hkv, S, Dqk, Dv, 0, softmax_scale};
-  hipError_t e = zyfa::launch_attn_fwd_bf16(a, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(ZYFA_ERR_LAUNCH, "attention launch failed: %s", hipGetErrorString(e));
+  return attn_bf16(q, k, v, o, lse, B, Hq, Hkv, S, S, 0, 0, S, Dqk, Dv, softmax_scale, stream);
+}
+
+zyfa_status zyfa_attn_fwd_fp8_range(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_scale,
+                                    const float* k_scale, const float* v_scale, int scale_block, uint16_t* o,
+                                    float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int q_offset, int k_begin,
+                                    int k_end, int Dqk, int Dv, float softmax_scale, int lean, void* stream) {
+  if (lean != 0 && lean != 1) return fail(ZYFA_ERR_INVALID_ARGUMENT, "lean must be 0 or 1");
+  return attn_fp8(q, k, v, q_scale, k_scale, v_scale, scale_block, o, lse, B, Hq, Hkv, Sq, Skv, q_offset, k_begin,
+                  k_end, Dqk, Dv, softmax_scale, stream, lean == 1);
+}
+
+zyfa_status zyfa_attn_fwd_bf16_range(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                                     float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int q_offset, int k_begin,
+                                     int k_end, int Dqk, int Dv, float softmax_scale, void* stream) {
+  return attn_bf16(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, q_offset, k_begin, k_end, Dqk, Dv, softmax_scale, stream);
+}
+
+zyfa_status zyfa_attn_merge(const uint16_t* o_parts, const float* lse_parts, int n_parts, uint16_t* o, float* lse,
+                            long long rows, int Dv, void* stream) {
+  if (!o_parts || !lse_parts || !o) return fail(ZYFA_ERR_INVALID_ARGUMENT, "o_parts, lse_parts and o must be non-null");
+  if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || (lse && !aligned16(lse)))
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  if (n_parts <= 0 || rows <= 0)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "n_parts and rows must be positive (got %d, %lld)", n_parts, rows);
+  if (Dv != 64 && Dv != 128 && Dv != 256 && Dv != 512)
+    return fail(ZYFA_ERR_UNSUPPORTED, "Dv = %d is not supported; use 64, 128, 256 or 512", Dv);
+  if ((long long)n_parts * rows * Dv > kMaxElems) return fail(ZYFA_ERR_INVALID_ARGUMENT, "tensor too large");
+  if ((const void*)o == (const void*)o_parts || (const void*)o == (const void*)lse_parts ||
+      (lse && ((const void*)lse == (const void*)o_parts || (const void*)lse == (const void*)lse_parts ||
+               (const void*)lse == (const void*)o)))
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
+  zyfa::MergeArgs a{o_parts, lse_parts, n_parts, o, lse, rows, Dv};
+  hipError_t e = zyfa::launch_attn_merge(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ZYFA_ERR_LAUNCH, "merge launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

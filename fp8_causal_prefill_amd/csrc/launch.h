@@ -16,10 +16,17 @@ struct AttnArgs {
   const float* v_scale;
   uint16_t* o;
   float* lse;            // may be null
-  int B, Hq, Hkv, S, Dqk, Dv;
+  int B, Hq, Hkv;
+  int Sq, Skv;           // rows per head of Q / O / LSE, and of K / V
+  int q_offset;          // sequence position of query row 0
+  int k_begin, k_end;    // key window [k_begin, k_end); k_begin a multiple of kKeyTile
+  int Dqk, Dv;
   int scale_block;       // FP8 only
   float softmax_scale;
 };
+
+// keys per tile of the attention kernels: a key window must start on a tile boundary
+constexpr int kKeyTile = 64;
 
 // lean: probabilities as linear e4m3 codes instead of rounded exponentials
 hipError_t launch_attn_fwd_fp8(const AttnArgs& a, bool lean, hipStream_t stream);
@@ -34,5 +41,17 @@ struct QuantArgs {
 };
 
 hipError_t launch_quantize_fp8(const QuantArgs& a, hipStream_t stream);
+
+struct MergeArgs {
+  const uint16_t* o_parts;  // [n_parts, rows, Dv] bf16
+  const float* lse_parts;   // [n_parts, rows]
+  int n_parts;
+  uint16_t* o;              // [rows, Dv] bf16
+  float* lse;               // [rows], may be null
+  long long rows;
+  int Dv;                   // 64, 128, 256 or 512
+};
+
+hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t stream);
 
 }  // namespace zyfa

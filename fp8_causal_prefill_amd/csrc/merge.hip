@@ -1,0 +1,85 @@
+// Merge of partial attention results over disjoint key sets.
+//
+// Zyphra "Inference Wave 2", section on CSA dual-scope decode: when the keys of one
+// attention call are split into shards, each shard returns its partial output together
+// with the log-sum-exp of its scores, and one merge step turns the parts into the
+// result of a single pass over all keys. For parts p with (O_p, LSE_p) of one query row:
+//
+//     M = max_p LSE_p,  w_p = exp(LSE_p - M),  W = sum_p w_p
+//     O = sum_p w_p O_p / W,  LSE = M + ln W
+//
+// A part whose row saw no key has LSE_p = -inf and weight zero; a row that no part saw
+// gets O = 0, LSE = -inf.
+//
+// HBM-bound: each row reads n_parts * (2 Dv + 4) bytes and writes 2 Dv (+ 4) bytes. A
+// group of Dv / 8 consecutive lanes owns a row, each lane 8 output values (16 bytes), so
+// every load and store of a wave is one contiguous run.
+#include <math.h>
+
+#include "device.h"
+#include "launch.h"
+
+namespace zyfa {
+
+constexpr int kMergeThreads = 256;
+
+template <int LANES>  // lanes per row = Dv / 8
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const uint16_t* __restrict__ o_parts,
+                                                                   const float* __restrict__ lse_parts,
+                                                                   int n_parts, uint16_t* __restrict__ o,
+                                                                   float* __restrict__ lse, long long rows) {
+  constexpr int ROWS_PER_BLOCK = kMergeThreads / LANES;
+  constexpr int DV = 8 * LANES;
+  const int sub = threadIdx.x % LANES;
+  const long long stride = (long long)gridDim.x * ROWS_PER_BLOCK;
+  for (long long r = (long long)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / LANES; r < rows; r += stride) {
+    float m = -INFINITY;
+    for (int p = 0; p < n_parts; ++p) m = fmaxf(m, lse_parts[(long long)p * rows + r]);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float wsum = 0.0f;
+    if (m > -INFINITY) {
+      for (int p = 0; p < n_parts; ++p) {
+        const float w = expf(lse_parts[(long long)p * rows + r] - m);  // exp(-inf) = 0
+        wsum += w;
+        const uint4 x = *(const uint4*)(o_parts + ((long long)p * rows + r) * DV + 8 * sub);
+        const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = fmaf(w, __uint_as_float(xw[i] << 16), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(w, __uint_as_float(xw[i] & 0xffff0000u), acc[2 * i + 1]);
+        }
+      }
+    }
+    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+    uint4 y;
+    y.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    y.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    y.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+    y.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+    *(uint4*)(o + r * DV + 8 * sub) = y;
+    if (lse != nullptr && sub == 0) lse[r] = wsum > 0.0f ? m + logf(wsum) : -INFINITY;
+  }
+}
+
+template <int LANES>
+static hipError_t launch_merge_t(const MergeArgs& a, hipStream_t stream) {
+  constexpr int ROWS_PER_BLOCK = kMergeThreads / LANES;
+  const long long blocks = (a.rows + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+  // a grid-stride loop covers any row count; 8192 workgroups keep all 256 CUs busy
+  const unsigned grid = (unsigned)(blocks < 8192 ? blocks : 8192);
+  hipLaunchKernelGGL((attn_merge_kernel<LANES>), dim3(grid), dim3(kMergeThreads), 0, stream, a.o_parts,
+                     a.lse_parts, a.n_parts, a.o, a.lse, a.rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_merge(const MergeArgs& a, hipStream_t stream) {
+  switch (a.Dv) {
+    case 64: return launch_merge_t<8>(a, stream);
+    case 128: return launch_merge_t<16>(a, stream);
+    case 256: return launch_merge_t<32>(a, stream);
+    case 512: return launch_merge_t<64>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace zyfa

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define ZYFA_ABI_VERSION 1
+#define ZYFA_ABI_VERSION 2
 
 typedef enum zyfa_status {
   ZYFA_OK = 0,
@@ -163,6 +163,69 @@ zyfa_status zyfa_attn_fwd_fp8_lean(const uint8_t* q, const uint8_t* k, const uin
  */
 zyfa_status zyfa_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
                                int B, int Hq, int Hkv, int S, int Dqk, int Dv, float softmax_scale, void* stream);
+
+/*
+ * zyfa_attn_fwd_fp8_range / zyfa_attn_fwd_bf16_range -- causal attention of a chunk of
+ * query rows against a window of keys.
+ *
+ * Source: ZYFA page, Introduction and "Methodology and Limitations" (the causal forward
+ * pass: a query attends to keys at positions up to its own); Zyphra "Inference Wave 2",
+ * section on CSA dual-scope decode (keys split into shards, each returning a partial
+ * output and its log-sum-exp, merged by zyfa_attn_merge). The same kernels as
+ * zyfa_attn_fwd_fp8 / _bf16, which are the case Sq = Skv = S, q_offset = 0,
+ * [k_begin, k_end) = [0, S).
+ *
+ *   q            [B, Hq, Sq, Dqk]: query row i is the token at sequence position
+ *                q_offset + i.
+ *   k, v         [B, Hkv, Skv, Dqk] and [B, Hkv, Skv, Dv]: key j is the token at
+ *                position j.
+ *   q_scale      FP8: [B, Hq, ceil(Sq / scale_block)], blocks of the rows of q;
+ *   k_scale, v_scale  FP8: [B, Hkv, ceil(Skv / scale_block)], blocks of positions.
+ *   o, lse       out: [B, Hq, Sq, Dv] bfloat16 and (may be NULL) [B, Hq, Sq] float32.
+ *   k_begin, k_end  the key window: key j is visible to query row i iff
+ *                k_begin <= j < k_end and j <= q_offset + i. 0 <= k_begin < k_end <= Skv
+ *                and k_begin is a multiple of 64.
+ *   q_offset     >= 0, with q_offset + Sq <= 2^30.
+ *   lean         FP8 only: 0 = probabilities as in zyfa_attn_fwd_fp8, 1 = as in
+ *                zyfa_attn_fwd_fp8_lean.
+ *
+ * A row that sees no key of the window (q_offset + i < k_begin) gets O = 0 and
+ * LSE = -inf, the form zyfa_attn_merge expects of a part that holds none of the row's
+ * keys. Chunked prefill over a cached prefix is q_offset = prefix length with the window
+ * [0, q_offset + Sq); a split of the keys into windows gives parts that zyfa_attn_merge
+ * combines. Other rules (pointers, alignment, streams, errors) as zyfa_attn_fwd_fp8;
+ * invalid windows or offsets are ZYFA_ERR_INVALID_ARGUMENT.
+ */
+zyfa_status zyfa_attn_fwd_fp8_range(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_scale,
+                                    const float* k_scale, const float* v_scale, int scale_block, uint16_t* o,
+                                    float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int q_offset, int k_begin,
+                                    int k_end, int Dqk, int Dv, float softmax_scale, int lean, void* stream);
+
+zyfa_status zyfa_attn_fwd_bf16_range(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                                     float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int q_offset, int k_begin,
+                                     int k_end, int Dqk, int Dv, float softmax_scale, void* stream);
+
+/*
+ * zyfa_attn_merge -- combine partial attention results over disjoint key sets.
+ *
+ * Source: Zyphra "Inference Wave 2", section on CSA dual-scope decode: each key shard
+ * produces a partial output and a log-sum-exp statistic, and a merge step combines them
+ * into the answer of one pass over all keys.
+ *
+ *   o_parts      [n_parts, rows, Dv] bfloat16: the parts' outputs (e.g. n_parts stacked
+ *                [B, H, S, Dv] tensors, rows = B * H * S).
+ *   lse_parts    [n_parts, rows] float32, natural log; -inf marks a row for which the
+ *                part saw no key (its output is then ignored).
+ *   o            out: [rows, Dv] bfloat16 (round-to-nearest-even).
+ *   lse          out, may be NULL: [rows] float32.
+ *   Dv           64, 128, 256 or 512; n_parts >= 1; rows >= 1.
+ *
+ * Per row: M = max_p LSE_p, w_p = exp(LSE_p - M), O = sum_p w_p O_p / sum_p w_p,
+ * LSE = M + ln sum_p w_p, in float32; a row no part saw gets O = 0, LSE = -inf.
+ * Pointers: device, 16-byte aligned, outputs not aliasing inputs. Errors as above.
+ */
+zyfa_status zyfa_attn_merge(const uint16_t* o_parts, const float* lse_parts, int n_parts, uint16_t* o, float* lse,
+                            long long rows, int Dv, void* stream);
 
 #ifdef __cplusplus
 }

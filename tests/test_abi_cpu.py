@@ -36,14 +36,15 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"zyfa_abi_version", "zyfa_status_string", "zyfa_last_error", "zyfa_quantize_fp8",
-                          "zyfa_attn_fwd_fp8", "zyfa_attn_fwd_fp8_lean", "zyfa_attn_fwd_bf16"}
+                          "zyfa_attn_fwd_fp8", "zyfa_attn_fwd_fp8_lean", "zyfa_attn_fwd_bf16",
+                          "zyfa_attn_fwd_fp8_range", "zyfa_attn_fwd_bf16_range", "zyfa_attn_merge"}
     raw = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.zyfa_abi_version() == 1
+    assert lib.zyfa_abi_version() == 2
     assert lib.zyfa_status_string(0) == b"ZYFA_OK"
     assert lib.zyfa_status_string(1) == b"ZYFA_ERR_INVALID_ARGUMENT"
     assert lib.zyfa_status_string(2) == b"ZYFA_ERR_UNSUPPORTED"
@@ -87,6 +88,53 @@ def test_attention_argument_checks(lib, kw, expect):
 def test_fp8_scale_checks(lib, kw):
     assert fp8(lib, **kw) == INVALID
     assert fp8(lib, lean=True, **kw) == INVALID
+
+
+def fp8_range(lib, q=P, k=P2, v=P3, qs=P4, ks=P5, vs=P6, blk=128, o=P7, lse=None, B=1, Hq=4, Hkv=2, Sq=256, Skv=512,
+              q_offset=256, k_begin=0, k_end=512, Dqk=128, Dv=128, scale=0.088, lean=0):
+    return lib.zyfa_attn_fwd_fp8_range(q, k, v, qs, ks, vs, blk, o, lse, B, Hq, Hkv, Sq, Skv, q_offset, k_begin, k_end,
+                                       Dqk, Dv, scale, lean, None)
+
+
+def bf16_range(lib, q=P, k=P2, v=P3, o=P7, lse=None, B=1, Hq=4, Hkv=2, Sq=256, Skv=512, q_offset=256, k_begin=0,
+               k_end=512, Dqk=128, Dv=128, scale=0.088):
+    return lib.zyfa_attn_fwd_bf16_range(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, q_offset, k_begin, k_end, Dqk, Dv, scale,
+                                        None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID), (dict(o=MIS), INVALID), (dict(Sq=0), INVALID), (dict(Skv=0), INVALID),
+    (dict(q_offset=-1), INVALID), (dict(q_offset=(1 << 30) - 255), INVALID),
+    (dict(k_begin=-64), INVALID), (dict(k_begin=32), INVALID), (dict(k_begin=128, k_end=128), INVALID),
+    (dict(k_begin=192, k_end=100), INVALID), (dict(k_end=513), INVALID), (dict(k_end=0), INVALID),
+    (dict(Hq=6, Hkv=4), INVALID), (dict(scale=0.0), INVALID), (dict(Dqk=64, Dv=64), UNSUPPORTED),
+    (dict(o=P2), INVALID),  # output aliases k
+])
+def test_range_argument_checks(lib, kw, expect):
+    assert bf16_range(lib, **kw) == expect
+    assert lib.zyfa_last_error() != b""
+    assert fp8_range(lib, **kw) == expect
+    assert fp8_range(lib, lean=1, **kw) == expect
+
+
+@pytest.mark.parametrize("kw", [dict(qs=None), dict(vs=MIS), dict(blk=32), dict(lean=2), dict(lean=-1)])
+def test_fp8_range_scale_and_mode_checks(lib, kw):
+    assert fp8_range(lib, **kw) == INVALID
+
+
+def merge(lib, op=P, lp=P2, n=2, o=P3, lse=None, rows=1000, Dv=128):
+    return lib.zyfa_attn_merge(op, lp, n, o, lse, rows, Dv, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(op=None), INVALID), (dict(lp=None), INVALID), (dict(o=None), INVALID), (dict(op=MIS), INVALID),
+    (dict(lse=MIS), INVALID), (dict(n=0), INVALID), (dict(rows=0), INVALID), (dict(rows=-3), INVALID),
+    (dict(Dv=100), UNSUPPORTED), (dict(Dv=192), UNSUPPORTED), (dict(o=P), INVALID), (dict(lse=P2), INVALID),
+    (dict(lse=P3), INVALID), (dict(n=1 << 20, rows=1 << 20), INVALID),
+])
+def test_merge_argument_checks(lib, kw, expect):
+    assert merge(lib, **kw) == expect
+    assert lib.zyfa_last_error() != b""
 
 
 def quant(lib, x=P, bf=0, codes=P2, scales=P3, B=1, H=2, S=100, D=128, blk=64, had=0):
