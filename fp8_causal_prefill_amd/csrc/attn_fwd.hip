@@ -10,8 +10,10 @@
 //    by hand.
 //  * "Precision and Underflow of FP8 Probabilities" and "Per-Block Scaling and
 //    Normalization by the Rounded Row Sum": probabilities of each (query row,
-//    64-key block) are multiplied by a power of two that puts the block maximum in
-//    [1, 2) before rounding to e4m3; the scaled FP8 matrix instruction divides it
+//    64-key block) are multiplied by a power of two that puts the block maximum near
+//    1 (here in [128, 256), kPHeadroom binades above [1, 2), which keeps 7 more binades
+//    of small weights out of e4m3's subnormal range) before rounding to e4m3; the scaled
+//    FP8 matrix instruction divides it
 //    back out; each row is normalised by the sum of exactly the rounded values
 //    that multiply V, computed by one more matrix instruction.
 //  * "Lean P": probabilities are formed in base 2, p = 2^x with x the score minus
@@ -61,6 +63,12 @@ constexpr float kLazyThreshold = 8.0f;
 // Exponent reference of a row that has seen no key yet: finite, so that masked scores give
 // probabilities of exactly zero, and far below any score, so the first visible key moves it.
 constexpr float kRefEmpty = -1e30f;
+// FP8 probabilities of a (query row, 64-key block) are scaled by a power of two that puts
+// the block maximum in [2^kPHeadroom, 2^(kPHeadroom + 1)): every e4m3 binade above the
+// subnormal range carries the same relative precision, and the headroom keeps weights down
+// to 2^-(6 + kPHeadroom) of their block maximum out of it (down to 2^-6 without headroom),
+// while the block maximum stays below 256 and e4m3's largest value, 448.
+constexpr int kPHeadroom = 7;
 // Lean probabilities: code = round(8 y + kLeanBias) for p = 2^y. 56 is the code of 1.0;
 // the linear code overestimates 2^y inside each binade by 0 to 0.69 codes (mean 0.46),
 // and subtracting that mean minimises the error of the normalised output.
@@ -447,7 +455,13 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     auto sidx = [&](int tile) { return min((p.k_begin + tile * C::BN) >> p.scale_shift, p.nbk - 1); };
     float ks_next = kscale[sidx(1)];
     float vs_next = vscale[sidx(1)];
-    auto block_exp = [&](float xmax) { return (int)fmaxf(floorf(xmax - m_ref), -126.0f); };
+    // scale exponent e of a block whose row maximum is xmax (base 2): p = 2^(s c - m_ref - e)
+    // puts the maximum in [2^kPHeadroom, 2^(kPHeadroom + 1)); 2^-e is the E8M0 scale code
+    // 127 + e, kept >= 1 (a block more than 119 binades below the reference holds weights
+    // that round to zero either way)
+    auto block_exp = [&](float xmax) {
+      return (int)fmaxf(floorf(xmax - m_ref) - (float)kPHeadroom, -126.0f);
+    };
 
     float rv_cur;
     int sv_cur;
@@ -470,8 +484,8 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     // exponential, then round-to-nearest-even conversion. Lean mode ("Lean P: Linear
     // Approximation of the FP8 Code"): the code of 2^y is close to 8 y + 56 (eight codes
     // per binade, 56 = 1.0), so it is taken as round-half-even(8 y + kLeanBias) clamped to
-    // [0, 255] (y < 1 keeps it below 64): one FMA and one conversion per value instead of
-    // an exponential and half a conversion.
+    // [0, 255] (y < kPHeadroom + 1 keeps it at most 120, below e4m3's NaN code 127): one
+    // FMA and one conversion per value instead of an exponential and half a conversion.
     auto p_codes = [&](const v16f& sv, int j0, float c, float bias) -> int {
       if constexpr (LEAN) {
         const float c8 = 8.0f * c, b8 = fmaf(-8.0f, bias, kLeanBias);
@@ -552,7 +566,8 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       if (has_next) qk((t + 1) % C::NBUF, s_next);
       pv(p_prev, sp_prev, sv_prev, (t + C::NBUF - 1) % C::NBUF);
 
-      // p = 2^(s*c - m_ref - eb): the block maximum lands in [1, 2), rounded to e4m3
+      // p = 2^(s*c - m_ref - eb): the block maximum lands in [2^kPHeadroom, 2^(kPHeadroom+1)),
+      // rounded to e4m3
       const float bias = m_ref + (float)eb_cur;
       int pw[8];
 #pragma unroll

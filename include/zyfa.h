@@ -118,7 +118,9 @@ zyfa_status zyfa_quantize_fp8(const void* x, int x_is_bf16, uint8_t* codes, floa
  * Supported: (Dqk, Dv) in {(128, 128), (192, 128)}, Hq % Hkv == 0, any S >= 1.
  * Method: scores on the FP8 matrix cores; probabilities are formed with a
  * base-2 exponential, and every (query row, 64-key block) of probabilities is
- * multiplied by a power of two that puts its largest value in [1, 2) before the
+ * multiplied by a power of two that puts its largest value in [128, 256) (the block
+ * maximum "close to 1" of the source, moved 7 binades up so that weights down to 2^-13
+ * of it stay out of e4m3's subnormal range) before the
  * round-to-nearest-even conversion to e4m3; the power of two is divided back out
  * by the scaled FP8 matrix instruction. Each row is normalised by the sum of the
  * rounded probabilities that multiply V, so the output is a weighted average
@@ -138,7 +140,7 @@ zyfa_status zyfa_attn_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t*
  *
  * Same arguments, layouts, scales, errors and output as zyfa_attn_fwd_fp8. Only the
  * probabilities differ: with y = s*c - bias the base-2 exponent of a probability after
- * its block scaling (y < 1), its code is round-half-even(8 y + 55.54) clamped to
+ * its block scaling (y < 8), its code is round-half-even(8 y + 55.54) clamped to
  * [0, 255] instead of the round-to-nearest-even e4m3 code of 2^y: one fused multiply-add
  * and one conversion per score, no exponential. The normalisation still uses the sum of
  * exactly these codes' values, so outputs remain weighted averages. An opt-in fast mode:

@@ -273,18 +273,17 @@ def test_rising_scores_move_the_reference(Dqk):
     print(f"rising Dqk={Dqk}: fp8 rel-L2 {e_exact:.3e}, lean {e_lean:.3e}")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(o_lean))
     assert e_exact <= FP8_BAR
-    # Attention here rests on a few dozen keys whose weights fall 5 binades per tile, so
-    # the lean code's per-weight distortion (up to ~4 %) averages out less than on
-    # Gaussian inputs: measured 1.63x the exact kernel's error at Dqk = 128 (3.55e-2,
-    # above the FP8 bar, which is why lean probabilities are an opt-in mode)
-    assert e_lean <= min(2.0 * e_exact + 1e-3, 4e-2)
+    # Attention here rests on a few dozen keys whose weights fall 5 binades per tile. Much
+    # of a row's weight then lies several binades below its block's maximum; with the block
+    # maximum scaled into [128, 256) it stays in e4m3's normal range (down to 2^-13 of the
+    # maximum), where the lean code is off by a bounded factor: measured 1.19x the exact
+    # kernel's error (1.63x, 3.55e-2, when the maximum was scaled into [1, 2) and such
+    # weights were subnormal)
+    assert e_lean <= min(LEAN_FACTOR * e_exact + 1e-3, FP8_BAR)
     assert np.max(np.abs(lse - rlse)) < 0.062
-    # In rows with one dominant key, much of the remaining weight lies 6-7 binades below
-    # its block's maximum, where e4m3 is subnormal and the linear code is far off (-30 %
-    # at 2^-6.5, zero below 2^-7; rounding keeps values down to ~2^-9.5): a float64
-    # emulation of the lean codes on these inputs gives log-sum-exp errors up to 0.11
-    # (exact codes: 0.018), the kernel 0.14
-    assert np.max(np.abs(lse_lean - rlse)) < 0.2
+    # a lean code of a normal e4m3 value is off by at most 0.083 in log; weights under
+    # 2^-13 of their block's maximum (subnormal) sum to less than 2^-7 of it: < 0.1
+    assert np.max(np.abs(lse_lean - rlse)) < 0.1
     ob, lseb = gpu_bf16(q, k, v, scale)
     rob, rlseb, _ = oracle_bf16(q, k, v, scale)
     e_bf16 = rel_l2(ob, rob)
