@@ -862,9 +862,16 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       op[0] = read_op(0);
       op[1] = read_op(1);
       float mx = MASKED ? -INFINITY : mx0, xmax = 0.0f, p_even = 0.0f;
+      // Waves w and w + 4 share a SIMD and leave each barrier together; the arbiter favours
+      // the older one, which then waits at the next barrier while the younger finishes its
+      // slots alone (measured in cycle stamps: about a fifth of the iteration). The younger
+      // wave takes precedence for the first three quarters of the slots (1.3-1.6 % faster,
+      // A/B on one box).
+      if (wave_u >= 4) __builtin_amdgcn_s_setprio(1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma clang loop unroll(full)
       for (int i = 0; i < NSLOTB; ++i) {
+        if (i == 3 * NSLOTB / 4) __builtin_amdgcn_s_setprio(0);
         if (i + 2 < NSLOTB) op[(i + 2) % 3] = read_op(i + 2);
         if constexpr (MASKED) {
           if (i == 0) mask_nb(sc, t);
