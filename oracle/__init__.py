@@ -32,7 +32,8 @@ Modules:
 * ``fp8``       - e4m3 (OCP E4M3FN) decode / round-to-nearest-even encode,
                   bfloat16 round-to-nearest-even.
 * ``quant``     - per-(batch, head, token-block) absmax quantizer and the
-                  Sylvester Hadamard rotation.
+                  Hadamard rotation (Sylvester order 128; order 192 as the
+                  Kronecker product of Paley's order-12 matrix and Sylvester's 16).
 * ``attention`` - fp64 causal attention with GQA and log-sum-exp, over all
                   rows or a chosen subset of query rows; the same for a chunk of
                   query rows against a window of keys, and the merge of partial
@@ -46,11 +47,11 @@ Hadamard matrix, torch's float64 scaled_dot_product_attention).
 
 from .fp8 import (E4M3_MAX, e4m3_decode, e4m3_encode, bf16_round, bf16_bits_to_f64,
                   f32_to_bf16_bits)
-from .quant import quantize_blocks, dequantize_blocks, hadamard_matrix, hadamard_rotate
+from .quant import quantize_blocks, dequantize_blocks, hadamard_matrix, hadamard_rotate, paley_hadamard_12
 from .attention import causal_attention, causal_probs, merge_partials, window_attention
 
 __all__ = [
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "bf16_round", "bf16_bits_to_f64", "f32_to_bf16_bits",
-    "quantize_blocks", "dequantize_blocks", "hadamard_matrix", "hadamard_rotate",
+    "quantize_blocks", "dequantize_blocks", "hadamard_matrix", "hadamard_rotate", "paley_hadamard_12",
     "causal_attention", "causal_probs", "window_attention", "merge_partials",
 ]

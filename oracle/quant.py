@@ -63,20 +63,48 @@ def dequantize_blocks(codes, scales, block):
     return e4m3_decode(codes) * per_token[..., None]
 
 
+def paley_hadamard_12():
+    """Hadamard matrix of order 12 from Paley's first construction over GF(11) (11 = 3 mod 4):
+    chi is the quadratic character of GF(11) (chi(0) = 0, +1 on the nonzero squares, -1
+    elsewhere), Q[i][j] = chi(j - i) its Jacobsthal matrix, S the 12 x 12 matrix with a zero
+    corner, ones along the rest of the first row, minus ones down the rest of the first
+    column and Q below and to the right; H = I + S. Entries +-1, H H^T = 12 I."""
+    q = 11
+    squares = {(x * x) % q for x in range(1, q)}
+
+    def chi(x):
+        x %= q
+        return 0 if x == 0 else (1 if x in squares else -1)
+
+    s = np.zeros((12, 12))
+    s[0, 1:] = 1.0
+    s[1:, 0] = -1.0
+    s[1:, 1:] = [[chi(j - i) for j in range(q)] for i in range(q)]
+    return np.eye(12) + s
+
+
 def hadamard_matrix(n):
-    """Sylvester Hadamard matrix of order n (a power of two), entries +-1, unnormalized:
-    H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]]."""
-    if n < 1 or n & (n - 1):
-        raise ValueError("order must be a power of two")
-    h = np.ones((1, 1))
-    while h.shape[0] < n:
-        h = np.block([[h, h], [h, -h]])
-    return h
+    """Hadamard matrix of order n, entries +-1, unnormalized.
+
+    n a power of two: Sylvester's H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]].
+    n = 12 * 2^k (192 for the MLA head dimension): the Kronecker product of the order-12
+    Paley matrix and the Sylvester matrix of order 2^k, element (m 2^k + b, m' 2^k + b') =
+    P12[m, m'] * H[b, b'], itself a Hadamard matrix of order n."""
+    if n >= 1 and not n & (n - 1):
+        h = np.ones((1, 1))
+        while h.shape[0] < n:
+            h = np.block([[h, h], [h, -h]])
+        return h
+    if n % 12 == 0 and n >= 12 and not (n // 12) & (n // 12 - 1):
+        return np.kron(paley_hadamard_12(), hadamard_matrix(n // 12))
+    raise ValueError("order must be a power of two or 12 times one")
 
 
 def hadamard_rotate(x):
     """Rotate the last axis of ``x`` by the orthonormal Hadamard matrix H_n / sqrt(n),
-    in float64: y = x @ (H_n / sqrt(n)). H_n is symmetric, so this is also H x."""
+    in float64: y = x @ (H_n / sqrt(n)), a row vector times the matrix (for powers of two
+    H_n is symmetric; the order-192 matrix is not). Rotating both Q and K leaves Q K^T
+    unchanged (H H^T = n I)."""
     x = np.asarray(x, dtype=np.float64)
     n = x.shape[-1]
     return x @ (hadamard_matrix(n) / np.sqrt(n))

@@ -11,7 +11,8 @@ import pytest
 import scipy.linalg
 import torch
 
-from oracle import quantize_blocks, dequantize_blocks, hadamard_matrix, hadamard_rotate, e4m3_decode
+from oracle import (quantize_blocks, dequantize_blocks, hadamard_matrix, hadamard_rotate, e4m3_decode,
+                    paley_hadamard_12)
 
 
 def _x(shape, seed=0):
@@ -87,8 +88,39 @@ def test_hadamard_matches_scipy_and_is_orthogonal():
         h = hadamard_matrix(n)
         assert np.array_equal(h, scipy.linalg.hadamard(n))
         assert np.array_equal(h @ h.T, n * np.eye(n))
-    with pytest.raises(ValueError):
-        hadamard_matrix(96)
+    for n in (6, 20, 100, 200):
+        with pytest.raises(ValueError):
+            hadamard_matrix(n)
+
+
+@pytest.mark.parametrize("n", [12, 24, 192])
+def test_order_12_times_power_of_two_is_hadamard(n):
+    # the defining properties: entries +-1 and mutually orthogonal rows (H H^T = n I), so
+    # H / sqrt(n) is orthonormal; a Paley matrix of order 12 has a first row of ones
+    h = hadamard_matrix(n)
+    assert set(np.unique(h)) == {-1.0, 1.0}
+    assert np.array_equal(h @ h.T, n * np.eye(n))
+    assert np.array_equal(h.T @ h, n * np.eye(n))
+    p12 = paley_hadamard_12()
+    assert np.array_equal(p12[0], np.ones(12)) and np.array_equal(p12 @ p12.T, 12 * np.eye(12))
+    # not a Sylvester matrix in disguise: no power-of-two Hadamard matrix has order 12
+    assert not np.array_equal(p12, p12.T)
+
+
+def test_order_192_rotation_preserves_scores_and_spreads_outliers():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((40, 192))
+    k = rng.standard_normal((40, 192))
+    q[:, 150] *= 15
+    k[:, 150] *= 15
+    qr, kr = hadamard_rotate(q), hadamard_rotate(k)
+    assert np.allclose(qr @ kr.T, q @ k.T, rtol=0, atol=1e-10)
+    assert np.allclose(np.linalg.norm(qr, axis=1), np.linalg.norm(q, axis=1), rtol=1e-12)
+    for j in (0, 17, 150, 191):
+        e = np.zeros(192)
+        e[j] = 1.0
+        assert np.allclose(np.abs(hadamard_rotate(e)), 1 / np.sqrt(192))
+    assert np.abs(kr).max() < np.abs(k).max() / 3
 
 
 def test_hadamard_rotation_preserves_scores_and_spreads_outliers():
