@@ -284,6 +284,13 @@ def other_workloads(names, steps, warmup, torch, zy):
         qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
         del q, k, v
         rec = {"shape": f"B={w.B} Hq={w.Hq} Hkv={w.Hkv} S={w.S} Dqk={w.Dqk} Dv={w.Dv}", "flops": w.flops}
+        # the Q quantization pass, without and with the Hadamard rotation (HBM-bound: 4 bytes
+        # read and 1 written per element, plus one scale per block)
+        qbytes = qd.numel() * 5 + qd.numel() // (w.Dqk * w.scale_block) * 4
+        for had in (False, True):
+            ms, med = time_kernel(lambda: zy.quantize_fp8(qd, w.scale_block, had), steps, warmup, stream, torch)
+            rec["quantize_q" + ("_hadamard" if had else "")] = {"ms": med, "gbs": qbytes / med / 1e6,
+                                                                  "frac_of_hbm": qbytes / med / 1e6 / PEAK_HBM_GBS}
         for had in ((False, True) if w.dist == "activation" else (False,)):
             qc, qs = zy.quantize_fp8(qd, w.scale_block, had)
             kc, ks = zy.quantize_fp8(kd, w.scale_block, had)

@@ -97,7 +97,7 @@ zyfa_status zyfa_quantize_fp8(const void* x, int x_is_bf16, uint8_t* codes, floa
     return fail(ZYFA_ERR_INVALID_ARGUMENT, "scale_block must be 64 or 128 (got %d)", scale_block);
   if ((long long)B * H * S * D > kMaxElems) return fail(ZYFA_ERR_INVALID_ARGUMENT, "tensor too large");
   if (D != 128 && D != 192) return fail(ZYFA_ERR_UNSUPPORTED, "D = %d is not supported; use 128 or 192", D);
-  if (hadamard && D != 128) return fail(ZYFA_ERR_UNSUPPORTED, "the Hadamard rotation requires D = 128");
+
   const long long nb = (S + scale_block - 1) / scale_block;
   if (nb * B * H > 0x7FFFFFFFLL) return fail(ZYFA_ERR_UNSUPPORTED, "grid too large");
   if ((const void*)codes == x || (const void*)scales == x || (const void*)scales == (const void*)codes)

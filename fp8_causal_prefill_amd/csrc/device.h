@@ -158,6 +158,30 @@ __device__ __forceinline__ void wait_vmem() {
 #endif
 }
 
+// The value of lane l ^ M, for M in {1, 2, 4, 8, 16}, without a trip through the LDS
+// crossbar (which __shfl_xor takes): M = 1, 2 are DPP quad permutations; M = 4, 8 pick a
+// DPP row shift down or up by M (within each 16-lane row) by the lane's bit M; M = 16 swaps
+// the odd 16-lane rows of one copy with the even rows of another (v_permlane16_swap) and
+// takes, per row, the copy that holds the partner row.
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  if constexpr (M == 1) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  } else if constexpr (M == 2) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  } else if constexpr (M == 4 || M == 8) {
+    const int up = __builtin_amdgcn_update_dpp(x, x, 0x100 + M, 0xF, 0xF, false);    // row_shl: lane l + M
+    const int down = __builtin_amdgcn_update_dpp(x, x, 0x110 + M, 0xF, 0xF, false);  // row_shr: lane l - M
+    return __builtin_bit_cast(float, (__lane_id() & M) ? down : up);
+  } else {
+    static_assert(M == 16, "lane_xor: M must be 1, 2, 4, 8 or 16");
+    const auto r = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+    // r[0]: rows (0, 0, 2, 2) of x; r[1]: rows (1, 1, 3, 3)
+    return __builtin_bit_cast(float, (__lane_id() & 16) ? r[0] : r[1]);
+  }
+}
+
 // max of a value across lanes i and i+32.
 __device__ __forceinline__ float max_across_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),

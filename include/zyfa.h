@@ -82,7 +82,10 @@ const char* zyfa_last_error(void);
  *   scales       out: [B, H, nb] float32, nb = ceil(S / scale_block).
  *   scale_block  tokens per scale: 64 or 128.
  *   hadamard     0: none. 1: first rotate every row of D values by the orthonormal
- *                Sylvester Hadamard matrix H_D / sqrt(D) (requires D == 128).
+ *                Hadamard matrix H_D / sqrt(D), as the row vector times the matrix:
+ *                Sylvester's matrix for D = 128; for D = 192 (the MLA shape) the
+ *                Kronecker product of Paley's order-12 matrix (first construction over
+ *                GF(11)) and Sylvester's of order 16.
  *
  * For each (b, h, token block): amax = max |y| over the block's tokens and all D
  * channels (y = x, or the rotated row); s = the least power of two with
@@ -90,7 +93,7 @@ const char* zyfa_last_error(void);
  * scaled FP8 matrix instruction applies exactly; code = round-to-nearest-even
  * e4m3 of the exact quotient y / s, saturated to +-448. Without rotation the
  * result is bit-exact to that definition; with rotation y is computed in float32
- * by a fast Walsh-Hadamard transform.
+ * (a fast Walsh-Hadamard transform; for D = 192 also the order-12 factor as sums).
  * The dequantized value of an element is decode(code) * s.
  */
 zyfa_status zyfa_quantize_fp8(const void* x, int x_is_bf16, uint8_t* codes, float* scales, int B, int H,

@@ -144,7 +144,8 @@ def quant(lib, x=P, bf=0, codes=P2, scales=P3, B=1, H=2, S=100, D=128, blk=64, h
 @pytest.mark.parametrize("kw,expect", [
     (dict(x=None), INVALID), (dict(codes=None), INVALID), (dict(scales=None), INVALID), (dict(x=MIS), INVALID),
     (dict(bf=2), INVALID), (dict(had=3), INVALID), (dict(B=0), INVALID), (dict(S=0), INVALID), (dict(D=0), INVALID),
-    (dict(blk=100), INVALID), (dict(D=64), UNSUPPORTED), (dict(D=192, had=1), UNSUPPORTED), (dict(codes=P), INVALID),
+    (dict(blk=100), INVALID), (dict(D=64), UNSUPPORTED), (dict(D=64, had=1), UNSUPPORTED), (dict(codes=P), INVALID),
+    (dict(D=192, had=2), INVALID),
 ])
 def test_quantize_argument_checks(lib, kw, expect):
     assert quant(lib, **kw) == expect

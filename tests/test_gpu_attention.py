@@ -83,6 +83,25 @@ def test_fp8_activation_like_with_and_without_rotation():
         assert err <= FP8_BAR
 
 
+def test_fp8_mla_activation_like_with_and_without_rotation():
+    # the MLA shape (Dqk 192) with outlier channels: parity against the oracle on the codes
+    # the kernel read, in both cases; against attention on the unquantized inputs the
+    # order-192 rotation must cut the input-quantization error (its purpose)
+    w = custom(1, 4, 4, 640, 192, 128, dist="activation", scale_block=128, wid=710)
+    q, k, v = generate(w, seed=0)
+    exact, _ = causal_attention(q, k, v, w.softmax_scale)
+    errs = {}
+    for hadamard in (False, True):
+        _case("mla act", hadamard=hadamard)
+        o, _, parts = gpu_fp8(q, k, v, 128, hadamard=hadamard)
+        ro, _ = oracle_attention_from_codes(parts, 128, w.softmax_scale)
+        err = rel_l2(o, ro)
+        errs[hadamard] = rel_l2(o, exact)
+        print(f"fp8 mla act hadamard={hadamard} rel-L2 {err:.3e}, vs unquantized inputs {errs[hadamard]:.3e}")
+        assert err <= FP8_BAR
+    assert errs[True] < 0.7 * errs[False]
+
+
 def _fp8_call(qc, kc, vc, qs, ks, vs, block, scale=None):
     o, lse = zy.attn_fwd_fp8(qc, kc, vc, qs, ks, vs, block, scale, return_lse=True)
     torch.cuda.synchronize()

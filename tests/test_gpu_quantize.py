@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import fp8_causal_prefill_amd as zy
 from oracle import quantize_blocks, hadamard_rotate, e4m3_decode
 from workloads import custom, generate
 from tests.paths import gpu_quantize, to_dev
@@ -56,10 +57,11 @@ def test_quantize_zero_block_and_extremes():
     assert np.array_equal(codes.cpu().numpy(), rc)
 
 
-@pytest.mark.parametrize("S,block", [(128, 64), (333, 128)])
-def test_quantize_hadamard(S, block):
-    _print_case(S=S, block=block)
-    w = custom(1, 2, 2, S, 128, 128, dist="activation", wid=400 + S)
+@pytest.mark.parametrize("S,block,D", [(128, 64, 128), (333, 128, 128), (128, 64, 192), (333, 128, 192),
+                                       (64, 128, 192)])
+def test_quantize_hadamard(S, block, D):
+    _print_case(S=S, block=block, D=D)
+    w = custom(1, 2, 2, S, D, 128, dist="activation", wid=400 + S)
     x, _, _ = generate(w, seed=4)
     codes, scales = gpu_quantize(x, block, hadamard=True)
     codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
@@ -79,3 +81,18 @@ def test_quantize_hadamard(S, block):
     assert np.all(err <= half_ulp * (1 + 1e-5) + np.abs(t) * 1e-6)
     mismatch = np.mean(codes != rc)
     assert mismatch < 1e-3, mismatch
+
+
+def test_quantize_hadamard_192_bf16_input():
+    _print_case(D=192, bf16=True)
+    w = custom(1, 3, 3, 200, 192, 128, dist="activation", wid=470)
+    x, _, _ = generate(w, seed=5)
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    codes, scales = zy.quantize_fp8(xb.to("cuda"), 64, True)
+    codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
+    y = hadamard_rotate(xb.float().numpy())  # the bf16 values the kernel read, rotated exactly
+    s = np.repeat(scales.astype(np.float64), 64, axis=2)[:, :, :200, None]
+    t = y / s
+    err = np.abs(e4m3_decode(codes) - t)
+    half_ulp = np.maximum(np.abs(t) * 2.0 ** -4, 2.0 ** -10)
+    assert np.all(err <= half_ulp * (1 + 1e-5) + np.abs(t) * 1e-6)
