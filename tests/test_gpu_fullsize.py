@@ -105,3 +105,54 @@ def test_full_size_bf16(wname):
         ref_heads.append(ro[0, 0])
         got_heads.append(bf16_from_f64(o[0, hq, torch.from_numpy(rows).to(dev)]))
     _check(f"{wname} bf16", got_heads, ref_heads, rows_e, rows_l, BARS["bf16"])
+
+
+def test_full_size_range_chunk_and_split_kv():
+    """The range measurements of the benchmark at the headline shape (32K GQA, FP8 exact):
+    the second half of the sequence as a chunk against its prefix, and the keys split into
+    [0, S/2) and [S/2, S) merged by zyfa_attn_merge. Checked on sampled rows of two heads
+    against the oracle (the chunk also bit for bit against the full call's rows)."""
+    from oracle import merge_partials, window_attention
+    w = WORKLOADS["gqa32k"]
+    print("case: gqa32k range chunk + split-KV", flush=True)
+    q, k, v = generate(w, seed=0)
+    dev = "cuda"
+    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    del q, k, v
+    blk, S = w.scale_block, w.S
+    qc, qs = zy.quantize_fp8(qd, blk)
+    kc, ks = zy.quantize_fp8(kd, blk)
+    vc, vs = zy.quantize_fp8(vd, blk)
+    del qd, kd, vd
+    half = S // 2
+    o_full, l_full = zy.attn_fwd_fp8(qc, kc, vc, qs, ks, vs, blk, w.softmax_scale, return_lse=True)
+    o_chunk, l_chunk = zy.attn_fwd_fp8_range(qc[:, :, half:].contiguous(), kc, vc, qs[:, :, half // blk:].contiguous(),
+                                             ks, vs, blk, half, 0, S, w.softmax_scale, return_lse=True)
+    parts = [zy.attn_fwd_fp8_range(qc, kc, vc, qs, ks, vs, blk, 0, lo, hi, w.softmax_scale, return_lse=True)
+             for lo, hi in ((0, half), (half, S))]
+    o_m, l_m = zy.attn_merge(torch.stack([p[0] for p in parts]), torch.stack([p[1] for p in parts]), return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_chunk, o_full[:, :, half:]) and torch.equal(l_chunk, l_full[:, :, half:])
+    # chunk rows: the first 256 of the chunk and 24 spread over it; merged output: the
+    # first 256 rows of the sequence, which see only the first window, and 24 spread
+    rows_c_e = np.arange(256)
+    rows_c_l = _late_rows(S - half, seed=2)
+    rows_m_l = _late_rows(S, seed=3)
+    group = w.Hq // w.Hkv
+    ref_c, got_c, ref_m, got_m = [], [], [], []
+    for hq in (0, w.Hq - 1):
+        hk = hq // group
+        deq = [dequantize_blocks(c[0:1, h:h + 1].cpu().numpy(), s[0:1, h:h + 1].cpu().numpy(), blk)
+               for c, s, h in ((qc, qs, hq), (kc, ks, hk), (vc, vs, hk))]
+        rows_c = np.concatenate([rows_c_e, rows_c_l])
+        rc, _ = window_attention(deq[0][:, :, half:], deq[1], deq[2], w.softmax_scale, q_offset=half, rows=rows_c)
+        ref_c.append(rc[0, 0])
+        got_c.append(bf16_from_f64(o_chunk[0, hq, torch.from_numpy(rows_c).to(dev)]))
+        rows_m = np.concatenate([np.arange(256), rows_m_l])
+        pr = [window_attention(deq[0], deq[1], deq[2], w.softmax_scale, k_begin=lo, k_end=hi, rows=rows_m)
+              for lo, hi in ((0, half), (half, S))]
+        rm, _ = merge_partials(np.stack([p[0] for p in pr]), np.stack([p[1] for p in pr]))
+        ref_m.append(rm[0, 0])
+        got_m.append(bf16_from_f64(o_m[0, hq, torch.from_numpy(rows_m).to(dev)]))
+    _check("gqa32k chunk", got_c, ref_c, rows_c_e, rows_c_l, BARS["fp8"])
+    _check("gqa32k split-KV merged", got_m, ref_m, np.arange(256), rows_m_l, BARS["fp8"])
