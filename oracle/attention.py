@@ -143,3 +143,30 @@ def merge_partials(o_parts, lse_parts):
     o[seen] = (np.einsum("p...,p...d->...d", w, o_parts)[seen]) / wsum[seen][:, None]
     lse = np.where(seen, m + np.log(np.where(seen, wsum, 1.0)), -np.inf)
     return o, lse
+
+
+def varlen_attention(q, k, v, scale, cu_seqlens, rows=None):
+    """Causal attention over a batch of sequences of different lengths, packed along the
+    token axis, in float64 (the ZYFA page's "Future Work" lists batches of variable length;
+    each sequence is the page's causal prefill on its own).
+
+    q: [Hq, T, Dqk], k: [Hkv, T, Dqk], v: [Hkv, T, Dv]; sequence i occupies tokens
+    cu_seqlens[i] .. cu_seqlens[i+1] - 1 of every head, and its query rows attend causally
+    to its own keys only. Tokens outside every sequence get O = 0 and LSE = -inf.
+    ``rows``: None, or packed token indices to compute (returned in that order).
+    Returns (o [Hq, R, Dv], lse [Hq, R])."""
+    q = np.asarray(q, dtype=np.float64)
+    Hq, T, _ = q.shape
+    cu = [int(c) for c in cu_seqlens]
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.zeros((Hq, rows.shape[0], np.asarray(v).shape[2]))
+    lse = np.full((Hq, rows.shape[0]), -np.inf)
+    for s0, s1 in zip(cu[:-1], cu[1:]):
+        sel = np.flatnonzero((rows >= s0) & (rows < s1))
+        if s1 <= s0 or sel.size == 0:
+            continue
+        oi, li = causal_attention(q[None, :, s0:s1], np.asarray(k)[None, :, s0:s1], np.asarray(v)[None, :, s0:s1],
+                                  scale, rows=rows[sel] - s0)
+        o[:, sel] = oi[0]
+        lse[:, sel] = li[0]
+    return o, lse

@@ -152,3 +152,32 @@ def test_merge_invariants():
     # log-sum-exp values far outside exp's range
     mh, lh = merge_partials(np.stack([o[0], o[1]]), np.stack([np.full(R, 2000.0), np.full(R, 2000.0)]))
     assert np.allclose(mh, (o[0] + o[1]) / 2, rtol=0, atol=1e-13) and np.allclose(lh, 2000 + math.log(2))
+
+
+def test_varlen_is_each_sequence_on_its_own():
+    # three sequences of different lengths packed with gaps between them: each equals the
+    # causal oracle on its own slice (mpmath-pinned), gaps are 0 / -inf, and no sequence
+    # sees another's keys (changing one sequence's K/V leaves the others bit for bit)
+    from oracle import varlen_attention
+    rng = np.random.default_rng(11)
+    Hq, Hkv, T, D = 4, 2, 400, 32
+    q = rng.standard_normal((Hq, T, D))
+    k = rng.standard_normal((Hkv, T, D))
+    v = rng.standard_normal((Hkv, T, D))
+    cu = [0, 64, 64, 192, 320, 390]  # an empty sequence, and tokens 390..399 outside all
+    o, lse = varlen_attention(q, k, v, 0.3, cu)
+    for s0, s1 in zip(cu[:-1], cu[1:]):
+        if s1 > s0:
+            ro, rl = causal_attention(q[None, :, s0:s1], k[None, :, s0:s1], v[None, :, s0:s1], 0.3)
+            assert np.array_equal(o[:, s0:s1], ro[0]) and np.array_equal(lse[:, s0:s1], rl[0])
+    assert np.all(o[:, 390:] == 0) and np.all(lse[:, 390:] == -np.inf)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 192:320] += 5.0
+    v2[:, 192:320] *= -1.0
+    o2, _ = varlen_attention(q, k2, v2, 0.3, cu)
+    assert np.array_equal(o2[:, :192], o[:, :192]) and np.array_equal(o2[:, 320:], o[:, 320:])
+    assert not np.allclose(o2[:, 192:320], o[:, 192:320])
+    # a row subset
+    rows = np.array([0, 63, 64, 250, 389, 395])
+    os_, ls_ = varlen_attention(q, k, v, 0.3, cu, rows=rows)
+    assert np.array_equal(os_, o[:, rows]) and np.array_equal(ls_, lse[:, rows])
