@@ -177,7 +177,10 @@ def test_varlen_is_each_sequence_on_its_own():
     o2, _ = varlen_attention(q, k2, v2, 0.3, cu)
     assert np.array_equal(o2[:, :192], o[:, :192]) and np.array_equal(o2[:, 320:], o[:, 320:])
     assert not np.allclose(o2[:, 192:320], o[:, 192:320])
-    # a row subset
+    # a row subset (the matrix products see other shapes: equal up to rounding order)
     rows = np.array([0, 63, 64, 250, 389, 395])
     os_, ls_ = varlen_attention(q, k, v, 0.3, cu, rows=rows)
-    assert np.array_equal(os_, o[:, rows]) and np.array_equal(ls_, lse[:, rows])
+    assert np.allclose(os_, o[:, rows], rtol=0, atol=1e-13)
+    assert np.array_equal(np.isfinite(ls_), np.isfinite(lse[:, rows]))
+    fin = np.isfinite(ls_)
+    assert np.allclose(ls_[fin], lse[:, rows][fin], rtol=0, atol=1e-13)
