@@ -13,7 +13,8 @@ Prints one JSON line. ``value`` is FP8 whole-step throughput; the attention kern
 alone is timed with HIP events on the stream it runs on and reported against the
 datasheet dense FP8 peak in ``roofline``; the opt-in lean-probability FP8 mode is
 reported in ``fp8_lean`` and BF16 in ``bf16``; ``range`` times the range entry points
-(chunked prefill, split-KV with the merge kernel and its HBM roofline). The CPU baseline times the fp64 oracle
+(chunked prefill, split-KV with the merge kernel and its HBM roofline) and ``varlen`` a
+packed batch of eight sequences of 256 to 16384 tokens on the same tensors. The CPU baseline times the fp64 oracle
 on a bounded sample (whole query heads, about 15 s) on the host cores; the heads it
 computed also give a full-size parity figure (``sampled_rel_l2_fp8``).
 
@@ -270,6 +271,26 @@ def range_paths(w, qc, kc, vc, qs, ks, vs, steps, warmup, stream, torch, zy):
     return rec
 
 
+VARLEN_LENGTHS = (16384, 8192, 4096, 2048, 1024, 512, 256, 256)
+
+
+def varlen_batch(w, qc, kc, vc, qs, ks, vs, steps, warmup, stream, torch, zy):
+    """The benchmark's tensors read as one packed batch of sequences of different lengths
+    (the varlen entry point, FP8 exact): [H, T, D] with T = S, split into VARLEN_LENGTHS
+    (which sum to 32768). FLOPs: 2 (Dqk + Dv) Hq L^2 / 2 per sequence of length L."""
+    lengths = VARLEN_LENGTHS
+    if sum(lengths) != w.S or w.B != 1:
+        return None
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device=qc.device)
+    o = torch.empty((w.Hq, w.S, w.Dv), dtype=torch.bfloat16, device=qc.device)
+    args = (qc[0], kc[0], vc[0], qs[0], ks[0], vs[0], w.scale_block, cu, max(lengths), w.softmax_scale)
+    ms, med = time_kernel(lambda: zy.attn_fwd_fp8_varlen(*args, o=o), steps, warmup, stream, torch)
+    flops = sum(2.0 * (w.Dqk + w.Dv) * w.Hq * n * n / 2 for n in lengths)
+    print(f"[bench] varlen batch {lengths}: {ms:.3f} ms", file=sys.stderr, flush=True)
+    return {"lengths": list(lengths), "heads": f"Hq={w.Hq} Hkv={w.Hkv} D={w.Dqk}", "ms": ms, "ms_median": med,
+            "tflops": flops / ms / 1e9, "frac_of_fp8_peak": flops / ms / 1e9 / PEAK_FP8}
+
+
 def other_workloads(names, steps, warmup, torch, zy):
     """Kernel throughput on the other benchmark shapes (4K MHA, 32K MLA, 16K activation-like
     with and without the Hadamard rotation of Q and K): FP8 exact and lean, and BF16.
@@ -509,6 +530,8 @@ def main():
     }
 
     if not args.no_range:
+        line["varlen"] = varlen_batch(w, qc, kc, vc, qs, ks, vs, max(args.steps // 5, 5), max(args.warmup // 10, 5),
+                                      stream, torch, zy)
         line["range"] = range_paths(w, qc, kc, vc, qs, ks, vs, max(args.steps // 5, 5), max(args.warmup // 10, 5), stream,
                                     torch, zy)
 

@@ -17,6 +17,9 @@ Functions mirror the C entry points:
   [k_begin, k_end) -> (o, lse or None)
 * ``attn_merge(o_parts, lse_parts)`` -> (o bfloat16, lse float32 or None): combine partial
   results over disjoint key sets
+* ``attn_fwd_fp8_varlen(q, k, v, q_scale, k_scale, v_scale, scale_block, cu_seqlens, max_seqlen)``
+  / ``attn_fwd_bf16_varlen``: a batch of sequences of different lengths packed as
+  [H, T, D] -> (o [Hq, T, Dv], lse or None)
 """
 
 import math
@@ -27,7 +30,7 @@ from . import _lib
 from ._lib import ZyfaError, load
 
 __all__ = ["quantize_fp8", "attn_fwd_fp8", "attn_fwd_bf16", "attn_fwd_fp8_range", "attn_fwd_bf16_range", "attn_merge",
-           "ZyfaError", "load", "abi_version"]
+           "attn_fwd_fp8_varlen", "attn_fwd_bf16_varlen", "ZyfaError", "load", "abi_version"]
 
 
 def abi_version() -> int:
@@ -222,4 +225,71 @@ def attn_merge(o_parts, lse_parts, o=None, lse=None, return_lse: bool = False):
             raise ValueError("lse has the wrong shape")
     st = load().zyfa_attn_merge(po_p, pl_p, P, po, plse, rows, Dv, _stream())
     _lib.check(st, "zyfa_attn_merge")
+    return o, lse
+
+
+def _varlen_common(q, k, v, cu_seqlens, max_seqlen, o, lse, return_lse):
+    Hq, T, Dqk = q.shape
+    Hkv, Tk, Dk = k.shape
+    if (Tk, Dk) != (T, Dqk) or tuple(v.shape[:2]) != (Hkv, T):
+        raise ValueError(f"inconsistent shapes q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    pcu = _dev(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    n_seqs = cu_seqlens.shape[0] - 1
+    Dv = v.shape[2]
+    if o is None:
+        o = torch.zeros((Hq, T, Dv), dtype=torch.bfloat16, device=q.device)
+    po = _dev(o, "o", torch.bfloat16, 3)
+    if tuple(o.shape) != (Hq, T, Dv):
+        raise ValueError("o has the wrong shape")
+    if lse is None and return_lse:
+        lse = torch.full((Hq, T), float("-inf"), dtype=torch.float32, device=q.device)
+    plse = None
+    if lse is not None:
+        plse = _dev(lse, "lse", torch.float32, 2)
+        if tuple(lse.shape) != (Hq, T):
+            raise ValueError("lse has the wrong shape")
+    return Hq, Hkv, T, Dqk, Dv, n_seqs, pcu, o, po, lse, plse
+
+
+def attn_fwd_fp8_varlen(q, k, v, q_scale, k_scale, v_scale, scale_block: int, cu_seqlens, max_seqlen: int,
+                        softmax_scale=None, o=None, lse=None, return_lse: bool = False, lean: bool = False):
+    """Causal attention over a packed batch: q [Hq, T, Dqk], k [Hkv, T, Dqk], v [Hkv, T, Dv]
+    (e4m3 codes, uint8), scales [H, ceil(T / scale_block)] (as quantize_fp8 writes them for
+    the tensors viewed as [1, H, T, D]); sequence i is tokens cu_seqlens[i] ..
+    cu_seqlens[i+1] - 1 (int32 device tensor; starts multiples of 64). Tokens outside every
+    sequence are left as they are in o / lse (zeros and -inf when this call allocates them).
+    Returns (o bfloat16 [Hq, T, Dv], lse or None)."""
+    pq = _dev(q, "q", torch.uint8, 3)
+    pk = _dev(k, "k", torch.uint8, 3)
+    pv = _dev(v, "v", torch.uint8, 3)
+    Hq, Hkv, T, Dqk, Dv, n_seqs, pcu, o, po, lse, plse = _varlen_common(q, k, v, cu_seqlens, max_seqlen, o, lse,
+                                                                        return_lse)
+    nb = (T + scale_block - 1) // scale_block if scale_block > 0 else 0
+    psq = _dev(q_scale, "q_scale", torch.float32, 2)
+    psk = _dev(k_scale, "k_scale", torch.float32, 2)
+    psv = _dev(v_scale, "v_scale", torch.float32, 2)
+    if tuple(q_scale.shape) != (Hq, nb) or tuple(k_scale.shape) != (Hkv, nb) or tuple(v_scale.shape) != (Hkv, nb):
+        raise ValueError("scale tensors have the wrong shape")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(Dqk)
+    st = load().zyfa_attn_fwd_fp8_varlen(pq, pk, pv, psq, psk, psv, scale_block, po, plse, pcu, n_seqs,
+                                         int(max_seqlen), Hq, Hkv, T, Dqk, Dv, float(softmax_scale), int(bool(lean)),
+                                         _stream())
+    _lib.check(st, "zyfa_attn_fwd_fp8_varlen")
+    return o, lse
+
+
+def attn_fwd_bf16_varlen(q, k, v, cu_seqlens, max_seqlen: int, softmax_scale=None, o=None, lse=None,
+                         return_lse: bool = False):
+    """attn_fwd_fp8_varlen on bfloat16 tensors. Returns (o bfloat16 [Hq, T, Dv], lse or None)."""
+    pq = _dev(q, "q", torch.bfloat16, 3)
+    pk = _dev(k, "k", torch.bfloat16, 3)
+    pv = _dev(v, "v", torch.bfloat16, 3)
+    Hq, Hkv, T, Dqk, Dv, n_seqs, pcu, o, po, lse, plse = _varlen_common(q, k, v, cu_seqlens, max_seqlen, o, lse,
+                                                                        return_lse)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(Dqk)
+    st = load().zyfa_attn_fwd_bf16_varlen(pq, pk, pv, po, plse, pcu, n_seqs, int(max_seqlen), Hq, Hkv, T, Dqk, Dv,
+                                          float(softmax_scale), _stream())
+    _lib.check(st, "zyfa_attn_fwd_bf16_varlen")
     return o, lse

@@ -48,8 +48,9 @@
 //    the mask is evaluated only on tiles that reach past a wave's first row.
 //  * Scheduling: workgroups are issued heaviest (last query tile) first; within a
 //    round over heads, consecutive workgroup ids (which the hardware spreads over
-//    the 8 XCDs) are mapped so that each XCD serves a contiguous range of heads,
-//    and query heads sharing a key/value head hit the same L2.
+//    the 8 XCDs) are mapped so that each XCD serves the same range of query heads of
+//    every batch entry: query heads sharing a key/value head hit the same L2, and
+//    batch entries of different lengths (a packed batch) spread over all XCDs.
 #include <math.h>
 
 #include <type_traits>
@@ -133,6 +134,11 @@ struct AttnParams {
   int d;        // position of query row 0 relative to k_begin
   int nbq, nbk, scale_shift, n_qtiles;  // scale blocks of Q and of K/V (1 << scale_shift tokens)
   float scale_log2;  // softmax_scale * log2(e)
+  // packed batch of sequences of different lengths (null otherwise): B sequences, sequence
+  // b being tokens cu_seqlens[b] .. cu_seqlens[b+1] - 1 of every head of [H, Sq = Skv, D]
+  // tensors, causal within itself; no sequence longer than max_seqlen
+  const int* cu_seqlens;
+  int max_seqlen;
 };
 
 template <bool FP8>
@@ -156,20 +162,51 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   const int wave = tid >> 6;
   const int h = lane >> 5;
   const int l32 = lane & 31;
-  const int Sq = p.Sq;
-  const int Sk = p.Sk;
 
   // ---- work item: (batch, query head, query tile), heaviest tile first ----
   const int NH = p.B * p.Hq;
   const int id = blockIdx.x;
   const int round = id / NH;
   const int in_round = id - round * NH;
+  // consecutive workgroup ids go to the 8 XCDs in turn: XCD x (id mod 8) serves query heads
+  // x Hq/8 .. (x + 1) Hq/8 - 1 of every batch entry, so that the query heads of a GQA group
+  // share one L2 and every batch entry (a sequence of its own length, in a packed batch) is
+  // spread over all XCDs
   int head = in_round;
-  if (NH % 8 == 0) head = (in_round & 7) * (NH >> 3) + (in_round >> 3);
+  if (p.Hq % 8 == 0) {
+    const int per = p.Hq >> 3, j = in_round >> 3, bb = j / per;
+    head = bb * p.Hq + (in_round & 7) * per + (j - bb * per);
+  } else if (NH % 8 == 0) {
+    head = (in_round & 7) * (NH >> 3) + (in_round >> 3);
+  }
   const int qt = p.n_qtiles - 1 - round;
   const int b = head / p.Hq;
   const int hq = head - b * p.Hq;
   const int hkv = hq / (p.Hq / p.Hkv);
+
+  // ---- the work item's geometry (wave-uniform) ----
+  int Sq = p.Sq, Sk = p.Sk, dpos = p.d, k_begin = p.k_begin;
+  size_t q_row0 = (size_t)(b * p.Hq + hq) * p.Sq;      // row of Q, O and LSE holding this head's query 0
+  size_t kv_row0 = (size_t)(b * p.Hkv + hkv) * p.Skv;  // row of K and V holding this head's key 0
+  int q_pos0 = 0;                                        // token position of query 0 (for Q scale blocks)
+  size_t q_sc0 = (size_t)(b * p.Hq + hq) * p.nbq;
+  size_t kv_sc0 = (size_t)(b * p.Hkv + hkv) * p.nbk;
+  if (p.cu_seqlens != nullptr) {
+    // packed batch: sequence b is tokens s0 .. s1 - 1 of every head, causal within itself.
+    // A malformed entry (a start off the key tile, decreasing, past the tensor, longer
+    // than max_seqlen) leaves the sequence unwritten, as do workgroups past its end.
+    const int s0 = p.cu_seqlens[b], s1 = p.cu_seqlens[b + 1];
+    if (s0 < 0 || (s0 & (C::BN - 1)) != 0 || s1 < s0 || s1 > p.Skv || s1 - s0 > p.max_seqlen) return;
+    Sq = Sk = s1 - s0;
+    dpos = 0;
+    k_begin = s0;
+    q_row0 = (size_t)hq * p.Sq + s0;
+    kv_row0 = (size_t)hkv * p.Skv;
+    q_pos0 = s0;
+    q_sc0 = (size_t)hq * p.nbq;
+    kv_sc0 = (size_t)hkv * p.nbk;
+    if (qt * C::BM >= Sq) return;
+  }
 
   const int q0_wg = qt * C::BM;
   const int q0 = q0_wg + __builtin_amdgcn_readfirstlane(wave) * 32;  // (wave-uniform)
@@ -177,38 +214,35 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   auto row_of_lane = [&] { return q0 + (int)(__lane_id() & 31); };
   const int my_q = row_of_lane();
   // last key of the window visible to this lane's row, and to the wave's first row
-  const int lim_q = min(p.d + my_q, Sk - 1);
-  const int lim_w = min(p.d + q0, Sk - 1);
+  const int lim_q = min(dpos + my_q, Sk - 1);
+  const int lim_w = min(dpos + q0, Sk - 1);
   // every wave runs the workgroup's trip count (key tiles up to the last one its last row
   // sees); tiles past a wave's rows are fully masked
-  const int last_key = min(p.d + min(q0_wg + C::BM, Sq) - 1, Sk - 1);
+  const int last_key = min(dpos + min(q0_wg + C::BM, Sq) - 1, Sk - 1);
   const int n = last_key < 0 ? 0 : last_key / C::BN + 1;
-
-  const size_t bh_q = (size_t)(b * p.Hq + hq);
-  const size_t bh_kv = (size_t)(b * p.Hkv + hkv);
 
   if (n == 0) {
     // no row of the workgroup sees a key of the window: O = 0, LSE = -inf
     if (my_q < Sq) {
-      uint16_t* orow = p.o + (bh_q * Sq + my_q) * C::DV;
+      uint16_t* orow = p.o + (q_row0 + my_q) * C::DV;
 #pragma unroll
       for (int d = 0; d < 4; ++d)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) *(uint2*)(orow + 32 * d + 8 * r4 + 4 * h) = uint2{0u, 0u};
-      if (p.lse != nullptr && h == 0) p.lse[bh_q * Sq + my_q] = -INFINITY;
+      if (p.lse != nullptr && h == 0) p.lse[q_row0 + my_q] = -INFINITY;
     }
     return;
   }
 
-  const char* kbase = p.k + (bh_kv * p.Skv + p.k_begin) * C::KROW;
-  const char* vbase = p.v + (bh_kv * p.Skv + p.k_begin) * C::VROW;
-  const float* kscale = p.k_scale + bh_kv * p.nbk;
-  const float* vscale = p.v_scale + bh_kv * p.nbk;
+  const char* kbase = p.k + (kv_row0 + k_begin) * C::KROW;
+  const char* vbase = p.v + (kv_row0 + k_begin) * C::VROW;
+  const float* kscale = p.k_scale + kv_sc0;
+  const float* vscale = p.v_scale + kv_sc0;
 
   // ---- Q operand (B of S^T = K Q^T): lane holds Q[my_q][c*KSTEP + h*KSTEP/2 ...] ----
   QOp<FP8> qreg[C::NKS];
   {
-    const char* qrow = p.q + (bh_q * Sq + min(my_q, Sq - 1)) * C::KROW;
+    const char* qrow = p.q + (q_row0 + min(my_q, Sq - 1)) * C::KROW;
 #pragma unroll
     for (int c = 0; c < C::NKS; ++c) {
       const char* src = qrow + (c * C::KSTEP + h * (C::KSTEP / 2)) * C::ESZ;
@@ -222,7 +256,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     }
   }
   float c_q = p.scale_log2;  // multiplies raw scores into base-2 units (times the tile's k scale for FP8)
-  if constexpr (FP8) c_q *= p.q_scale[bh_q * p.nbq + (min(q0, Sq - 1) >> p.scale_shift)];
+  if constexpr (FP8) c_q *= p.q_scale[q_sc0 + ((q_pos0 + min(q0, Sq - 1)) >> p.scale_shift)];
 
   // ---- direct global -> LDS staging ----
   // 16-byte position pos of a buffer is (column block, row r, stored chunk); the lane
@@ -396,7 +430,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   __syncthreads();
 
   // key tiles that every row of the workgroup sees whole (full tiles inside the window)
-  const int n_full = max(0, (min(p.d + q0_wg, Sk - 1) + 1) / C::BN);
+  const int n_full = max(0, (min(dpos + q0_wg, Sk - 1) + 1) / C::BN);
   // iterations t < n_steady need no causal mask on tile t+1 in any wave and prefetch
   // K_{t+2}: their bodies are branch-free and carry a fixed instruction schedule. The even
   // n_steady is at most n_full - 2, so every tile they fetch (t + 2 <= n_full - 1) is a
@@ -409,7 +443,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   __syncthreads();
   mask(sa, 0);
   float c_cur = c_q;
-  if constexpr (FP8) c_cur *= kscale[min(p.k_begin >> p.scale_shift, p.nbk - 1)];
+  if constexpr (FP8) c_cur *= kscale[min(k_begin >> p.scale_shift, p.nbk - 1)];
   // tile 0 holds the window's key 0, which every row at a position >= 0 sees: finite there
   float xmax0 = rowmax(sa) * c_cur;
   float m_ref = xmax0 > -INFINITY ? ceilf(xmax0) : kRefEmpty;
@@ -420,7 +454,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     const int my_q = row_of_lane();
     if (q0 >= Sq || my_q >= Sq) return;
     const float inv_l = l_sum > 0.0f ? 1.0f / l_sum : 0.0f;  // a row with no key: O = 0, LSE = -inf
-    uint16_t* orow = p.o + (bh_q * Sq + my_q) * C::DV;
+    uint16_t* orow = p.o + (q_row0 + my_q) * C::DV;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -430,7 +464,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
         w.y = pack_bf16x2(oacc[d][4 * r4 + 2] * inv_l, oacc[d][4 * r4 + 3] * inv_l);
         *(uint2*)(orow + 32 * d + 8 * r4 + 4 * h) = w;
       }
-    if (p.lse != nullptr && h == 0) p.lse[bh_q * Sq + my_q] = kLn2 * (m_ref + log2f(l_sum));
+    if (p.lse != nullptr && h == 0) p.lse[q_row0 + my_q] = kLn2 * (m_ref + log2f(l_sum));
   };
 
   if constexpr (FP8) {
@@ -452,7 +486,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     };
     // K and V scales of tile t+1 while iteration t runs; the loads for tile t+2 are
     // issued at the top of iteration t, ahead of the tile fills whose wait covers them
-    auto sidx = [&](int tile) { return min((p.k_begin + tile * C::BN) >> p.scale_shift, p.nbk - 1); };
+    auto sidx = [&](int tile) { return min((k_begin + tile * C::BN) >> p.scale_shift, p.nbk - 1); };
     float ks_next = kscale[sidx(1)];
     float vs_next = vscale[sidx(1)];
     // scale exponent e of a block whose row maximum is xmax (base 2): p = 2^(s c - m_ref - e)
@@ -977,7 +1011,9 @@ static hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   p.scale_shift = FP8 ? (a.scale_block == 64 ? 6 : 7) : 0;
   p.nbq = FP8 ? (a.Sq + a.scale_block - 1) / a.scale_block : 0;
   p.nbk = FP8 ? (a.Skv + a.scale_block - 1) / a.scale_block : 0;
-  p.n_qtiles = (a.Sq + C::BM - 1) / C::BM;
+  p.cu_seqlens = a.cu_seqlens;
+  p.max_seqlen = a.max_seqlen;
+  p.n_qtiles = ((a.cu_seqlens != nullptr ? a.max_seqlen : a.Sq) + C::BM - 1) / C::BM;
   p.scale_log2 = a.softmax_scale * kLog2e;
   const long long grid = (long long)p.n_qtiles * a.B * a.Hq;
   hipLaunchKernelGGL((attn_fwd_kernel<FP8, DQK, LEAN>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);

@@ -177,6 +177,56 @@ zyfa_status zyfa_attn_fwd_bf16_range(const uint16_t* q, const uint16_t* k, const
   return attn_bf16(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, q_offset, k_begin, k_end, Dqk, Dv, softmax_scale, stream);
 }
 
+static zyfa_status check_varlen(const int* cu_seqlens, int n_seqs, int max_seqlen, int Hq, int T) {
+  if (!cu_seqlens) return fail(ZYFA_ERR_INVALID_ARGUMENT, "cu_seqlens must be non-null");
+  if (((uintptr_t)cu_seqlens & 3u) != 0) return fail(ZYFA_ERR_INVALID_ARGUMENT, "cu_seqlens must be 4-byte aligned");
+  if (n_seqs <= 0 || max_seqlen <= 0)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "n_seqs and max_seqlen must be positive (got %d, %d)", n_seqs, max_seqlen);
+  if (max_seqlen > T) return fail(ZYFA_ERR_INVALID_ARGUMENT, "max_seqlen (%d) exceeds T (%d)", max_seqlen, T);
+  const long long n_qtiles = (max_seqlen + 127) / 128;
+  if (n_qtiles * n_seqs * Hq > 0x7FFFFFFFLL) return fail(ZYFA_ERR_UNSUPPORTED, "grid too large");
+  return ZYFA_OK;
+}
+
+zyfa_status zyfa_attn_fwd_fp8_varlen(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_scale,
+                                     const float* k_scale, const float* v_scale, int scale_block, uint16_t* o,
+                                     float* lse, const int* cu_seqlens, int n_seqs, int max_seqlen, int Hq, int Hkv,
+                                     int T, int Dqk, int Dv, float softmax_scale, int lean, void* stream) {
+  if (lean != 0 && lean != 1) return fail(ZYFA_ERR_INVALID_ARGUMENT, "lean must be 0 or 1");
+  zyfa_status st = check_attn_common(q, k, v, o, lse, 1, Hq, Hkv, T, T, 0, 0, T, Dqk, Dv, softmax_scale);
+  if (st != ZYFA_OK) return st;
+  st = check_varlen(cu_seqlens, n_seqs, max_seqlen, Hq, T);
+  if (st != ZYFA_OK) return st;
+  if (!q_scale || !k_scale || !v_scale) return fail(ZYFA_ERR_INVALID_ARGUMENT, "scale pointers must be non-null");
+  if (!aligned16(q_scale) || !aligned16(k_scale) || !aligned16(v_scale))
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  if (scale_block != 64 && scale_block != 128)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "scale_block must be 64 or 128 (got %d)", scale_block);
+  zyfa::AttnArgs a{q,  k, v,  q_scale, k_scale, v_scale, o,  lse,         n_seqs, Hq, Hkv,
+                   T,  T, 0,  0,       T,       Dqk,     Dv, scale_block, softmax_scale};
+  a.cu_seqlens = cu_seqlens;
+  a.max_seqlen = max_seqlen;
+  hipError_t e = zyfa::launch_attn_fwd_fp8(a, lean == 1, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ZYFA_ERR_LAUNCH, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+zyfa_status zyfa_attn_fwd_bf16_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                                      float* lse, const int* cu_seqlens, int n_seqs, int max_seqlen, int Hq, int Hkv,
+                                      int T, int Dqk, int Dv, float softmax_scale, void* stream) {
+  zyfa_status st = check_attn_common(q, k, v, o, lse, 1, Hq, Hkv, T, T, 0, 0, T, Dqk, Dv, softmax_scale);
+  if (st != ZYFA_OK) return st;
+  st = check_varlen(cu_seqlens, n_seqs, max_seqlen, Hq, T);
+  if (st != ZYFA_OK) return st;
+  zyfa::AttnArgs a{q, k, v, nullptr, nullptr, nullptr, o,  lse, n_seqs, Hq, Hkv,
+                   T, T, 0, 0,       T,       Dqk,     Dv, 0,   softmax_scale};
+  a.cu_seqlens = cu_seqlens;
+  a.max_seqlen = max_seqlen;
+  hipError_t e = zyfa::launch_attn_fwd_bf16(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ZYFA_ERR_LAUNCH, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 zyfa_status zyfa_attn_merge(const uint16_t* o_parts, const float* lse_parts, int n_parts, uint16_t* o, float* lse,
                             long long rows, int Dv, void* stream) {
   if (!o_parts || !lse_parts || !o) return fail(ZYFA_ERR_INVALID_ARGUMENT, "o_parts, lse_parts and o must be non-null");

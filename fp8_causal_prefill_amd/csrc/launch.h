@@ -23,6 +23,10 @@ struct AttnArgs {
   int Dqk, Dv;
   int scale_block;       // FP8 only
   float softmax_scale;
+  // packed batch (null otherwise): B sequences in [H, Sq = Skv, D] tensors, sequence b
+  // being tokens cu_seqlens[b] .. cu_seqlens[b+1] - 1 (device array of B + 1 ints)
+  const int* cu_seqlens = nullptr;
+  int max_seqlen = 0;
 };
 
 // keys per tile of the attention kernels: a key window must start on a tile boundary

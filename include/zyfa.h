@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define ZYFA_ABI_VERSION 2
+#define ZYFA_ABI_VERSION 3
 
 typedef enum zyfa_status {
   ZYFA_OK = 0,
@@ -209,6 +209,45 @@ zyfa_status zyfa_attn_fwd_fp8_range(const uint8_t* q, const uint8_t* k, const ui
 zyfa_status zyfa_attn_fwd_bf16_range(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                                      float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int q_offset, int k_begin,
                                      int k_end, int Dqk, int Dv, float softmax_scale, void* stream);
+
+/*
+ * zyfa_attn_fwd_fp8_varlen / zyfa_attn_fwd_bf16_varlen -- causal attention over a batch
+ * of sequences of different lengths, packed along the token axis.
+ *
+ * Source: ZYFA page, "Future Work" (batches of variable length) and Introduction (each
+ * sequence is a causal prefill of its own). The same kernels as zyfa_attn_fwd_fp8 /
+ * _bf16, with the batch index picking a sequence.
+ *
+ *   q            [Hq, T, Dqk]; k [Hkv, T, Dqk]; v [Hkv, T, Dv]: sequence i is tokens
+ *                cu_seqlens[i] .. cu_seqlens[i+1] - 1 of every head.
+ *   q_scale, k_scale, v_scale  FP8: [Hq, ceil(T / scale_block)] and
+ *                [Hkv, ceil(T / scale_block)], blocks of the packed token axis (the
+ *                layout zyfa_quantize_fp8 writes for a [1, H, T, D] tensor).
+ *   o, lse       out: [Hq, T, Dv] bfloat16 and (may be NULL) [Hq, T] float32. Tokens
+ *                after the last sequence (cu_seqlens[n_seqs] .. T - 1) are not written.
+ *   cu_seqlens   device array of n_seqs + 1 ints, non-decreasing, every entry but the
+ *                last a multiple of 64 (sequences start on a key tile), the last at most
+ *                T; no sequence longer than max_seqlen. To pack sequences of any length,
+ *                pad each but the last at its end to a multiple of 64 tokens (zeros keep
+ *                the FP8 block scales unaffected): under the causal rule a sequence's
+ *                real tokens never see the padding after them, so their outputs are
+ *                those of the unpadded sequence; the padding rows' outputs are computed
+ *                and meaningless. The array is read on the device: a sequence whose
+ *                entries break these rules is left unwritten (no error is reported).
+ *   max_seqlen   1 .. T; sizes the grid.
+ *   lean         FP8 only: 0 or 1, as in zyfa_attn_fwd_fp8_range.
+ *
+ * Other rules (pointers, alignment, streams, errors, supported head shapes) as
+ * zyfa_attn_fwd_fp8.
+ */
+zyfa_status zyfa_attn_fwd_fp8_varlen(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_scale,
+                                     const float* k_scale, const float* v_scale, int scale_block, uint16_t* o,
+                                     float* lse, const int* cu_seqlens, int n_seqs, int max_seqlen, int Hq, int Hkv,
+                                     int T, int Dqk, int Dv, float softmax_scale, int lean, void* stream);
+
+zyfa_status zyfa_attn_fwd_bf16_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                                      float* lse, const int* cu_seqlens, int n_seqs, int max_seqlen, int Hq, int Hkv,
+                                      int T, int Dqk, int Dv, float softmax_scale, void* stream);
 
 /*
  * zyfa_attn_merge -- combine partial attention results over disjoint key sets.

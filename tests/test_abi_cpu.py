@@ -37,14 +37,15 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"zyfa_abi_version", "zyfa_status_string", "zyfa_last_error", "zyfa_quantize_fp8",
                           "zyfa_attn_fwd_fp8", "zyfa_attn_fwd_fp8_lean", "zyfa_attn_fwd_bf16",
-                          "zyfa_attn_fwd_fp8_range", "zyfa_attn_fwd_bf16_range", "zyfa_attn_merge"}
+                          "zyfa_attn_fwd_fp8_range", "zyfa_attn_fwd_bf16_range", "zyfa_attn_merge",
+                          "zyfa_attn_fwd_fp8_varlen", "zyfa_attn_fwd_bf16_varlen"}
     raw = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.zyfa_abi_version() == 2
+    assert lib.zyfa_abi_version() == 3
     assert lib.zyfa_status_string(0) == b"ZYFA_OK"
     assert lib.zyfa_status_string(1) == b"ZYFA_ERR_INVALID_ARGUMENT"
     assert lib.zyfa_status_string(2) == b"ZYFA_ERR_UNSUPPORTED"
@@ -120,6 +121,34 @@ def test_range_argument_checks(lib, kw, expect):
 @pytest.mark.parametrize("kw", [dict(qs=None), dict(vs=MIS), dict(blk=32), dict(lean=2), dict(lean=-1)])
 def test_fp8_range_scale_and_mode_checks(lib, kw):
     assert fp8_range(lib, **kw) == INVALID
+
+
+def fp8_varlen(lib, q=P, k=P2, v=P3, qs=P4, ks=P5, vs=P6, blk=128, o=P7, lse=None, cu=0x80000, n=3, maxs=300,
+               Hq=4, Hkv=2, T=1000, Dqk=128, Dv=128, scale=0.088, lean=0):
+    return lib.zyfa_attn_fwd_fp8_varlen(q, k, v, qs, ks, vs, blk, o, lse, cu, n, maxs, Hq, Hkv, T, Dqk, Dv, scale, lean,
+                                        None)
+
+
+def bf16_varlen(lib, q=P, k=P2, v=P3, o=P7, lse=None, cu=0x80000, n=3, maxs=300, Hq=4, Hkv=2, T=1000, Dqk=128,
+                Dv=128, scale=0.088):
+    return lib.zyfa_attn_fwd_bf16_varlen(q, k, v, o, lse, cu, n, maxs, Hq, Hkv, T, Dqk, Dv, scale, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID), (dict(o=MIS), INVALID), (dict(cu=None), INVALID), (dict(cu=0x80002), INVALID),
+    (dict(n=0), INVALID), (dict(maxs=0), INVALID), (dict(maxs=1001), INVALID), (dict(T=0), INVALID),
+    (dict(Hq=6, Hkv=4), INVALID), (dict(scale=float("nan")), INVALID), (dict(Dqk=64, Dv=64), UNSUPPORTED),
+    (dict(o=P), INVALID),
+])
+def test_varlen_argument_checks(lib, kw, expect):
+    assert bf16_varlen(lib, **kw) == expect
+    assert lib.zyfa_last_error() != b""
+    assert fp8_varlen(lib, **kw) == expect
+
+
+@pytest.mark.parametrize("kw", [dict(qs=None), dict(blk=32), dict(lean=3)])
+def test_fp8_varlen_scale_and_mode_checks(lib, kw):
+    assert fp8_varlen(lib, **kw) == INVALID
 
 
 def merge(lib, op=P, lp=P2, n=2, o=P3, lse=None, rows=1000, Dv=128):

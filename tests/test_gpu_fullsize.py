@@ -156,3 +156,40 @@ def test_full_size_range_chunk_and_split_kv():
         got_m.append(bf16_from_f64(o_m[0, hq, torch.from_numpy(rows_m).to(dev)]))
     _check("gqa32k chunk", got_c, ref_c, rows_c_e, rows_c_l, BARS["fp8"])
     _check("gqa32k split-KV merged", got_m, ref_m, np.arange(256), rows_m_l, BARS["fp8"])
+
+
+def test_full_size_varlen_batch():
+    """The packed batch the benchmark times: the 32K GQA tensors read as [H, T, D] and split
+    into sequences of 16384 .. 256 tokens (FP8 exact). Sampled rows of two heads against the
+    oracle: the first 256 rows of the batch and 24 spread over it."""
+    from oracle import varlen_attention
+    import bench
+    w = WORKLOADS["gqa32k"]
+    print("case: gqa32k varlen batch", flush=True)
+    q, k, v = generate(w, seed=0)
+    dev = "cuda"
+    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    del q, k, v
+    blk = w.scale_block
+    qc, qs = zy.quantize_fp8(qd, blk)
+    kc, ks = zy.quantize_fp8(kd, blk)
+    vc, vs = zy.quantize_fp8(vd, blk)
+    del qd, kd, vd
+    lengths = bench.VARLEN_LENGTHS
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    o, _ = zy.attn_fwd_fp8_varlen(qc[0], kc[0], vc[0], qs[0], ks[0], vs[0], blk, torch.from_numpy(cu).to(dev),
+                                  max(lengths), w.softmax_scale)
+    torch.cuda.synchronize()
+    rows_e = np.arange(256)
+    rows_l = _late_rows(w.S, seed=4)
+    rows = np.concatenate([rows_e, rows_l])
+    group = w.Hq // w.Hkv
+    ref_heads, got_heads = [], []
+    for hq in (0, w.Hq - 1):
+        hk = hq // group
+        deq = [dequantize_blocks(c[0:1, h:h + 1].cpu().numpy(), s[0:1, h:h + 1].cpu().numpy(), blk)[0]
+               for c, s, h in ((qc, qs, hq), (kc, ks, hk), (vc, vs, hk))]
+        ro, _ = varlen_attention(deq[0], deq[1], deq[2], w.softmax_scale, cu, rows=rows)
+        ref_heads.append(ro[0])
+        got_heads.append(bf16_from_f64(o[hq, torch.from_numpy(rows).to(dev)]))
+    _check("gqa32k varlen", got_heads, ref_heads, rows_e, rows_l, BARS["fp8"])
