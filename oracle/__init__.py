@@ -37,8 +37,9 @@ Modules:
 * ``attention`` - fp64 causal attention with GQA and log-sum-exp, over all
                   rows or a chosen subset of query rows; the same for a chunk of
                   query rows against a window of keys, the merge of partial
-                  results over disjoint key sets, and batches of sequences of
-                  different lengths packed along the token axis.
+                  results over disjoint key sets, batches of sequences of
+                  different lengths packed along the token axis, and chunks of new
+                  tokens against a paged key/value cache.
 
 Every function here is pinned by tests that do not re-derive it from itself:
 printed code points, closed forms, invariants, brute force in 50-digit
@@ -49,10 +50,12 @@ Hadamard matrix, torch's float64 scaled_dot_product_attention).
 from .fp8 import (E4M3_MAX, e4m3_decode, e4m3_encode, bf16_round, bf16_bits_to_f64,
                   f32_to_bf16_bits)
 from .quant import quantize_blocks, dequantize_blocks, hadamard_matrix, hadamard_rotate, paley_hadamard_12
-from .attention import causal_attention, causal_probs, merge_partials, varlen_attention, window_attention
+from .attention import (causal_attention, causal_probs, gather_pages, merge_partials, paged_attention,
+                        varlen_attention, window_attention)
 
 __all__ = [
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "bf16_round", "bf16_bits_to_f64", "f32_to_bf16_bits",
     "quantize_blocks", "dequantize_blocks", "hadamard_matrix", "hadamard_rotate", "paley_hadamard_12",
     "causal_attention", "causal_probs", "window_attention", "merge_partials", "varlen_attention",
+    "gather_pages", "paged_attention",
 ]

@@ -170,3 +170,41 @@ def varlen_attention(q, k, v, scale, cu_seqlens, rows=None):
         o[:, sel] = oi[0]
         lse[:, sel] = li[0]
     return o, lse
+
+
+def gather_pages(cache, block_table, n_tokens):
+    """The first n_tokens tokens of one sequence from a paged cache, in float64: cache
+    [pages, H, P, D] holds P tokens of every head per page; block_table lists the
+    sequence's pages in order (logical page j of the sequence is cache[block_table[j]]).
+    Returns [H, n_tokens, D]."""
+    cache = np.asarray(cache)
+    P = cache.shape[2]
+    n_pages = -(-n_tokens // P)
+    pages = [cache[int(block_table[j])] for j in range(n_pages)]  # each [H, P, D]
+    return np.concatenate(pages, axis=1)[:, :n_tokens].astype(np.float64)
+
+
+def paged_attention(q, k_cache, v_cache, scale, cu_seqlens, kv_lens, block_table):
+    """Attention of chunks of new tokens against their sequences' cached keys, in float64
+    (prefill into a paged key/value cache; the ZYFA page's "Future Work" lists paged KV
+    caches). q: [Hq, T, Dqk], sequence i's new tokens being rows cu_seqlens[i] ..
+    cu_seqlens[i+1] - 1; they are the last L_i of the sequence's kv_lens[i] tokens, whose
+    keys and values sit in the pages block_table[i] of k_cache / v_cache
+    ([pages, Hkv, P, D]). Row r of the chunk is at position kv_lens[i] - L_i + r and sees
+    the sequence's keys up to it (window_attention). Rows outside every chunk get O = 0,
+    LSE = -inf. Returns (o [Hq, T, Dv], lse [Hq, T])."""
+    q = np.asarray(q, dtype=np.float64)
+    Hq, T, _ = q.shape
+    cu = [int(c) for c in cu_seqlens]
+    o = np.zeros((Hq, T, np.asarray(v_cache).shape[3]))
+    lse = np.full((Hq, T), -np.inf)
+    for i, (s0, s1) in enumerate(zip(cu[:-1], cu[1:])):
+        if s1 <= s0:
+            continue
+        n = int(kv_lens[i])
+        k = gather_pages(k_cache, block_table[i], n)
+        v = gather_pages(v_cache, block_table[i], n)
+        oi, li = window_attention(q[None, :, s0:s1], k[None], v[None], scale, q_offset=n - (s1 - s0))
+        o[:, s0:s1] = oi[0]
+        lse[:, s0:s1] = li[0]
+    return o, lse

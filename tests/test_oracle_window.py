@@ -184,3 +184,39 @@ def test_varlen_is_each_sequence_on_its_own():
     assert np.array_equal(np.isfinite(ls_), np.isfinite(lse[:, rows]))
     fin = np.isfinite(ls_)
     assert np.allclose(ls_[fin], lse[:, rows][fin], rtol=0, atol=1e-13)
+
+
+def test_paged_attention_is_the_chunk_against_its_gathered_prefix():
+    # sequences whose keys/values live in shuffled pages of a cache: each chunk equals the
+    # causal oracle's last rows on the contiguous sequence (pinned above), whatever the page
+    # order; rows outside every chunk are 0 / -inf
+    from oracle import paged_attention
+    rng = np.random.default_rng(12)
+    Hq, Hkv, D, P = 4, 2, 16, 64
+    lens = [200, 64, 130]        # tokens per sequence, cached
+    chunk = [72, 64, 1]          # new tokens per sequence (its last ones)
+    n_pages = sum(-(-n // P) for n in lens) + 3
+    perm = rng.permutation(n_pages)
+    seqs, tables, used = [], [], 0
+    k_cache = rng.standard_normal((n_pages, Hkv, P, D))
+    v_cache = rng.standard_normal((n_pages, Hkv, P, D))
+    for n in lens:
+        npg = -(-n // P)
+        pages = perm[used:used + npg]
+        used += npg
+        tables.append(np.concatenate([pages, np.zeros(8 - npg, dtype=np.int64)]))
+        seqs.append((np.concatenate([k_cache[p] for p in pages], axis=1)[:, :n],
+                     np.concatenate([v_cache[p] for p in pages], axis=1)[:, :n]))
+    cu = np.concatenate([[0], np.cumsum(chunk)])
+    T = cu[-1] + 5
+    full_q = [rng.standard_normal((Hq, n, D)) for n in lens]
+    q = np.zeros((Hq, T, D))
+    for i, (s0, s1) in enumerate(zip(cu[:-1], cu[1:])):
+        q[:, s0:s1] = full_q[i][:, lens[i] - chunk[i]:]
+    o, lse = paged_attention(q, k_cache, v_cache, 0.25, cu, lens, np.stack(tables))
+    for i, (s0, s1) in enumerate(zip(cu[:-1], cu[1:])):
+        k, v = seqs[i]
+        ro, rl = causal_attention(full_q[i][None], k[None], v[None], 0.25)
+        assert np.allclose(o[:, s0:s1], ro[0, :, lens[i] - chunk[i]:], rtol=0, atol=1e-12)
+        assert np.allclose(lse[:, s0:s1], rl[0, :, lens[i] - chunk[i]:], rtol=0, atol=1e-12)
+    assert np.all(o[:, cu[-1]:] == 0) and np.all(lse[:, cu[-1]:] == -np.inf)
