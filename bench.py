@@ -291,6 +291,57 @@ def varlen_batch(w, qc, kc, vc, qs, ks, vs, steps, warmup, stream, torch, zy):
             "tflops": flops / ms / 1e9, "frac_of_fp8_peak": flops / ms / 1e9 / PEAK_FP8}
 
 
+PAGE_SIZE = 128
+
+
+def paged_cache(w, kc, vc, ks, vs, torch):
+    """The benchmark's FP8 keys and values ([1, Hkv, S, D] codes, [1, Hkv, S / block] scales)
+    moved into a paged cache of PAGE_SIZE-token pages in a seeded random page order.
+    Returns (k pages, v pages, k scales, v scales, block table [1, S / PAGE_SIZE] int32)."""
+    from workloads import page_table
+    S, P, dev = w.S, PAGE_SIZE, kc.device
+    table, num_pages = page_table([S], P, seed=0)
+    bt = torch.from_numpy(table).to(dev)
+    idx = bt[0].long()
+
+    def to_pages(x, rows):  # [1, H, S', ...] -> [num_pages, H, rows per page, ...]
+        pages = x[0].reshape(x.shape[1], S // P, rows, *x.shape[3:]).transpose(0, 1)
+        cache = torch.zeros((num_pages, *pages.shape[1:]), dtype=x.dtype, device=dev)
+        cache[idx] = pages
+        return cache
+
+    blk = w.scale_block
+    return to_pages(kc, P), to_pages(vc, P), to_pages(ks, P // blk), to_pages(vs, P // blk), bt
+
+
+def paged_prefill(w, qc, kc, vc, qs, ks, vs, steps, warmup, stream, torch, zy):
+    """The paged entry point (FP8 exact) on the benchmark's keys and values in a shuffled
+    page cache (paged_cache): the whole sequence as one chunk (the plain call's work,
+    through the block table) and its second half as a chunk after a cached prefix of S / 2
+    tokens (the range chunk's work)."""
+    if w.B != 1 or w.S % PAGE_SIZE != 0:
+        return None
+    S, blk, dev = w.S, w.scale_block, qc.device
+    kp, vp, ksp, vsp, bt = paged_cache(w, kc, vc, ks, vs, torch)
+    o = torch.empty((w.Hq, S, w.Dv), dtype=torch.bfloat16, device=dev)
+    kvl = torch.tensor([S], dtype=torch.int32, device=dev)
+    rec = {"page_size": PAGE_SIZE, "num_pages": kp.shape[0], "order": "seeded random permutation"}
+    half = (S // 2) // blk * blk
+    for name, a, flops in (("whole", 0, w.flops),
+                           ("chunk", half, 2.0 * (w.Dqk + w.Dv) * w.Hq * (S * S - half * half) / 2)):
+        cu = torch.tensor([0, S - a], dtype=torch.int32, device=dev)
+        qa, qsa = qc[0, :, a:].contiguous(), qs[0, :, a // blk:].contiguous()
+        oa = o[:, :S - a] if a == 0 else torch.empty((w.Hq, S - a, w.Dv), dtype=torch.bfloat16, device=dev)
+        ms, med = time_kernel(lambda: zy.attn_fwd_fp8_paged(qa, kp, vp, qsa, ksp, vsp, blk, cu, kvl, bt, S - a,
+                                                            w.softmax_scale, o=oa), steps, warmup, stream, torch)
+        rec[name] = {"rows": S - a, "kv_len": S, "ms": ms, "ms_median": med, "tflops": flops / ms / 1e9,
+                     "frac_of_fp8_peak": flops / ms / 1e9 / PEAK_FP8}
+    print(f"[bench] paged: whole {rec['whole']['ms']:.3f} ms, chunk {rec['chunk']['ms']:.3f} ms",
+          file=sys.stderr, flush=True)
+    del kp, vp, ksp, vsp, o
+    return rec
+
+
 def other_workloads(names, steps, warmup, torch, zy):
     """Kernel throughput on the other benchmark shapes (4K MHA, 32K MLA, 16K activation-like
     with and without the Hadamard rotation of Q and K): FP8 exact and lean, and BF16.
@@ -348,7 +399,7 @@ def main():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-lean", action="store_true", help="skip the lean-probability FP8 mode")
     ap.add_argument("--no-others", action="store_true", help="skip the other workload shapes")
-    ap.add_argument("--no-range", action="store_true", help="skip the chunked-prefill and split-KV measurements")
+    ap.add_argument("--no-range", action="store_true", help="skip the varlen, chunked-prefill, split-KV and paged measurements")
     ap.add_argument("--sustain", type=float, default=4.0,
                     help="seconds of back-to-back launches per headline kernel, after 1.5 s of settling, "
                          "with clock and power telemetry (0: skip)")
@@ -534,6 +585,8 @@ def main():
                                       stream, torch, zy)
         line["range"] = range_paths(w, qc, kc, vc, qs, ks, vs, max(args.steps // 5, 5), max(args.warmup // 10, 5), stream,
                                     torch, zy)
+        line["paged"] = paged_prefill(w, qc, kc, vc, qs, ks, vs, max(args.steps // 5, 5), max(args.warmup // 10, 5),
+                                      stream, torch, zy)
 
     if not args.no_others:
         others = [n for n in ("mha4k", "mla32k", "act16k") if n != w.name]

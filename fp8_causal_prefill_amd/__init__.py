@@ -20,6 +20,10 @@ Functions mirror the C entry points:
 * ``attn_fwd_fp8_varlen(q, k, v, q_scale, k_scale, v_scale, scale_block, cu_seqlens, max_seqlen)``
   / ``attn_fwd_bf16_varlen``: a batch of sequences of different lengths packed as
   [H, T, D] -> (o [Hq, T, Dv], lse or None)
+* ``attn_fwd_fp8_paged(q, k_cache, v_cache, q_scale, k_cache_scale, v_cache_scale, scale_block,
+  cu_seqlens, kv_lens, block_table, max_seqlen)`` / ``attn_fwd_bf16_paged``: chunks of new
+  tokens (packed as in the varlen calls) against their sequences' keys in a paged cache
+  [pages, Hkv, page_size, D] -> (o [Hq, T, Dv], lse or None)
 """
 
 import math
@@ -30,7 +34,8 @@ from . import _lib
 from ._lib import ZyfaError, load
 
 __all__ = ["quantize_fp8", "attn_fwd_fp8", "attn_fwd_bf16", "attn_fwd_fp8_range", "attn_fwd_bf16_range", "attn_merge",
-           "attn_fwd_fp8_varlen", "attn_fwd_bf16_varlen", "ZyfaError", "load", "abi_version"]
+           "attn_fwd_fp8_varlen", "attn_fwd_bf16_varlen", "attn_fwd_fp8_paged", "attn_fwd_bf16_paged", "ZyfaError",
+           "load", "abi_version"]
 
 
 def abi_version() -> int:
@@ -292,4 +297,82 @@ def attn_fwd_bf16_varlen(q, k, v, cu_seqlens, max_seqlen: int, softmax_scale=Non
     st = load().zyfa_attn_fwd_bf16_varlen(pq, pk, pv, po, plse, pcu, n_seqs, int(max_seqlen), Hq, Hkv, T, Dqk, Dv,
                                           float(softmax_scale), _stream())
     _lib.check(st, "zyfa_attn_fwd_bf16_varlen")
+    return o, lse
+
+
+def _paged_common(q, k_cache, v_cache, cu_seqlens, kv_lens, block_table, max_seqlen, o, lse, return_lse):
+    Hq, T, Dqk = q.shape
+    num_pages, Hkv, page_size, Dk = k_cache.shape
+    if Dk != Dqk or tuple(v_cache.shape[:3]) != (num_pages, Hkv, page_size):
+        raise ValueError(f"inconsistent shapes q {tuple(q.shape)} k_cache {tuple(k_cache.shape)} "
+                         f"v_cache {tuple(v_cache.shape)}")
+    pcu = _dev(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    n_seqs = cu_seqlens.shape[0] - 1
+    pkl = _dev(kv_lens, "kv_lens", torch.int32, 1)
+    pbt = _dev(block_table, "block_table", torch.int32, 2)
+    if kv_lens.shape[0] != n_seqs or block_table.shape[0] != n_seqs:
+        raise ValueError("kv_lens and block_table need one entry / row per sequence")
+    max_pages = block_table.shape[1]
+    Dv = v_cache.shape[3]
+    if o is None:
+        o = torch.zeros((Hq, T, Dv), dtype=torch.bfloat16, device=q.device)
+    po = _dev(o, "o", torch.bfloat16, 3)
+    if tuple(o.shape) != (Hq, T, Dv):
+        raise ValueError("o has the wrong shape")
+    if lse is None and return_lse:
+        lse = torch.full((Hq, T), float("-inf"), dtype=torch.float32, device=q.device)
+    plse = None
+    if lse is not None:
+        plse = _dev(lse, "lse", torch.float32, 2)
+        if tuple(lse.shape) != (Hq, T):
+            raise ValueError("lse has the wrong shape")
+    return (Hq, Hkv, T, Dqk, Dv, n_seqs, num_pages, page_size, max_pages, pcu, pkl, pbt, o, po, lse, plse)
+
+
+def attn_fwd_fp8_paged(q, k_cache, v_cache, q_scale, k_cache_scale, v_cache_scale, scale_block: int, cu_seqlens,
+                       kv_lens, block_table, max_seqlen: int, softmax_scale=None, o=None, lse=None,
+                       return_lse: bool = False, lean: bool = False):
+    """Prefill of chunks of new tokens against a paged key/value cache. q [Hq, T, Dqk] (e4m3
+    codes) packs the chunks as in attn_fwd_fp8_varlen (cu_seqlens, int32, starts multiples of
+    64); k_cache / v_cache [num_pages, Hkv, page_size, D] (e4m3 codes), their scales
+    [num_pages, Hkv, page_size / scale_block] (quantize_fp8 of the cache as
+    [num_pages, Hkv, page_size, D]); block_table int32 [n_seqs, max_pages] lists each
+    sequence's pages; kv_lens int32 [n_seqs] its token count, of which its chunk is the
+    last. Row r of chunk i sits at position kv_lens[i] - L_i + r. Rows outside every chunk
+    are left as they are. Returns (o bfloat16 [Hq, T, Dv], lse or None)."""
+    pq = _dev(q, "q", torch.uint8, 3)
+    pk = _dev(k_cache, "k_cache", torch.uint8, 4)
+    pv = _dev(v_cache, "v_cache", torch.uint8, 4)
+    (Hq, Hkv, T, Dqk, Dv, n_seqs, num_pages, page_size, max_pages, pcu, pkl, pbt, o, po, lse,
+     plse) = _paged_common(q, k_cache, v_cache, cu_seqlens, kv_lens, block_table, max_seqlen, o, lse, return_lse)
+    nbq = (T + scale_block - 1) // scale_block if scale_block > 0 else 0
+    nbp = page_size // scale_block if scale_block > 0 else 0
+    psq = _dev(q_scale, "q_scale", torch.float32, 2)
+    psk = _dev(k_cache_scale, "k_cache_scale", torch.float32, 3)
+    psv = _dev(v_cache_scale, "v_cache_scale", torch.float32, 3)
+    if (tuple(q_scale.shape) != (Hq, nbq) or tuple(k_cache_scale.shape) != (num_pages, Hkv, nbp)
+            or tuple(v_cache_scale.shape) != (num_pages, Hkv, nbp)):
+        raise ValueError("scale tensors have the wrong shape")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(Dqk)
+    st = load().zyfa_attn_fwd_fp8_paged(pq, pk, pv, psq, psk, psv, scale_block, po, plse, pcu, pkl, pbt, n_seqs,
+                                        int(max_seqlen), max_pages, num_pages, page_size, Hq, Hkv, T, Dqk, Dv,
+                                        float(softmax_scale), int(bool(lean)), _stream())
+    _lib.check(st, "zyfa_attn_fwd_fp8_paged")
+    return o, lse
+
+
+def attn_fwd_bf16_paged(q, k_cache, v_cache, cu_seqlens, kv_lens, block_table, max_seqlen: int, softmax_scale=None,
+                        o=None, lse=None, return_lse: bool = False):
+    """attn_fwd_fp8_paged on bfloat16 tensors. Returns (o bfloat16 [Hq, T, Dv], lse or None)."""
+    pq = _dev(q, "q", torch.bfloat16, 3)
+    pk = _dev(k_cache, "k_cache", torch.bfloat16, 4)
+    pv = _dev(v_cache, "v_cache", torch.bfloat16, 4)
+    (Hq, Hkv, T, Dqk, Dv, n_seqs, num_pages, page_size, max_pages, pcu, pkl, pbt, o, po, lse,
+     plse) = _paged_common(q, k_cache, v_cache, cu_seqlens, kv_lens, block_table, max_seqlen, o, lse, return_lse)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(Dqk)
+    st = load().zyfa_attn_fwd_bf16_paged(pq, pk, pv, po, plse, pcu, pkl, pbt, n_seqs, int(max_seqlen), max_pages,
+                                         num_pages, page_size, Hq, Hkv, T, Dqk, Dv, float(softmax_scale), _stream())
+    _lib.check(st, "zyfa_attn_fwd_bf16_paged")
     return o, lse

@@ -30,6 +30,8 @@ _SIGNATURES = {
     "zyfa_attn_merge": ([_vp, _vp, _i, _vp, _vp, ctypes.c_longlong, _i, _vp], _i),
     "zyfa_attn_fwd_fp8_varlen": ([_vp] * 6 + [_i, _vp, _vp, _vp] + [_i] * 7 + [_f, _i, _vp], _i),
     "zyfa_attn_fwd_bf16_varlen": ([_vp] * 6 + [_i] * 7 + [_f, _vp], _i),
+    "zyfa_attn_fwd_fp8_paged": ([_vp] * 6 + [_i] + [_vp] * 5 + [_i] * 10 + [_f, _i, _vp], _i),
+    "zyfa_attn_fwd_bf16_paged": ([_vp] * 8 + [_i] * 10 + [_f, _vp], _i),
 }
 
 

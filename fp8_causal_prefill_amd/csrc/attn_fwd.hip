@@ -139,6 +139,13 @@ struct AttnParams {
   // tensors, causal within itself; no sequence longer than max_seqlen
   const int* cu_seqlens;
   int max_seqlen;
+  // paged key/value cache (PAGED kernels): K and V are [num_pages, Hkv, 1 << page_shift, D]
+  // and their FP8 scales [num_pages, Hkv, pages' scale blocks]; sequence b's logical page j
+  // is block_table[b * max_pages + j]; its kv_lens[b] tokens end with the chunk of new
+  // tokens that cu_seqlens gives (rows of Q, O, LSE, packed as in a varlen batch)
+  const int* block_table;
+  const int* kv_lens;
+  int max_pages, num_pages, page_shift;
 };
 
 template <bool FP8>
@@ -149,7 +156,7 @@ using QOp = typename std::conditional<FP8, v8i, v8bf>::type;
 // 16-key run) occupy 8 consecutive rows.
 __device__ __forceinline__ int fp8_vrow(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
-template <bool FP8, int DQK, bool LEAN>
+template <bool FP8, int DQK, bool LEAN, bool PAGED>
 __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(AttnParams p) {
   static_assert(FP8 || !LEAN, "lean probabilities are an FP8 mode");
   using C = Cfg<FP8, DQK>;
@@ -191,7 +198,23 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   int q_pos0 = 0;                                        // token position of query 0 (for Q scale blocks)
   size_t q_sc0 = (size_t)(b * p.Hq + hq) * p.nbq;
   size_t kv_sc0 = (size_t)(b * p.Hkv + hkv) * p.nbk;
-  if (p.cu_seqlens != nullptr) {
+  if constexpr (PAGED) {
+    // a chunk of new tokens (rows s0 .. s1 - 1 of the packed Q) that ends sequence b's
+    // kv_lens[b] cached tokens: row i sits at position kvl - L + i and sees keys up to it.
+    // Malformed entries leave the chunk unwritten, as for a packed batch.
+    const int s0 = p.cu_seqlens[b], s1 = p.cu_seqlens[b + 1], kvl = p.kv_lens[b];
+    if (s0 < 0 || (s0 & (C::BN - 1)) != 0 || s1 <= s0 || s1 > p.Sq || s1 - s0 > p.max_seqlen || kvl < s1 - s0 ||
+        kvl > (p.max_pages << p.page_shift))
+      return;
+    Sq = s1 - s0;
+    Sk = kvl;
+    dpos = kvl - Sq;
+    k_begin = 0;
+    q_row0 = (size_t)hq * p.Sq + s0;
+    q_pos0 = s0;
+    q_sc0 = (size_t)hq * p.nbq;
+    if (qt * C::BM >= Sq) return;
+  } else if (p.cu_seqlens != nullptr) {
     // packed batch: sequence b is tokens s0 .. s1 - 1 of every head, causal within itself.
     // A malformed entry (a start off the key tile, decreasing, past the tensor, longer
     // than max_seqlen) leaves the sequence unwritten, as do workgroups past its end.
@@ -238,6 +261,16 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   const char* vbase = p.v + (kv_row0 + k_begin) * C::VROW;
   const float* kscale = p.k_scale + kv_sc0;
   const float* vscale = p.v_scale + kv_sc0;
+  // PAGED: the row of the cache ([pages x Hkv x page rows] rows of D) holding key tile t's
+  // first key; a tile never straddles pages (a page holds whole tiles). Page indices are
+  // clamped to the table and the cache, so a malformed table reads wrong rows, never past
+  // the tensors.
+  auto page_row0 = [&](int t) -> size_t {
+    const int pos = t * C::BN;
+    const int j = min(pos >> p.page_shift, p.max_pages - 1);
+    const int page = min(max(p.block_table[(size_t)b * p.max_pages + j], 0), p.num_pages - 1);
+    return (((size_t)page * p.Hkv + hkv) << p.page_shift) + (pos & ((1 << p.page_shift) - 1));
+  };
 
   // ---- Q operand (B of S^T = K Q^T): lane holds Q[my_q][c*KSTEP + h*KSTEP/2 ...] ----
   QOp<FP8> qreg[C::NKS];
@@ -291,19 +324,31 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   for (int i = 0; i < C::VCHUNKS; ++i) v_src[i] = v_pos_row(i) * C::VROW + v_pos_off(i);
   const uint32_t k_lds = lds_address(kring), v_lds = lds_address(vring);
 
+  // first K / V byte of key tile t (t0 = t * BN)
+  auto k_tile = [&](int t) -> const char* {
+    if constexpr (PAGED) return p.k + page_row0(t) * C::KROW;
+    else return kbase + (size_t)(t * C::BN) * C::KROW;
+  };
+  auto v_tile = [&](int t) -> const char* {
+    if constexpr (PAGED) return p.v + page_row0(t) * C::VROW;
+    else return vbase + (size_t)(t * C::BN) * C::VROW;
+  };
   auto fill_k = [&](int t, int buf) {
     const int t0 = t * C::BN;
     const uint32_t dst = k_lds + buf * C::KBUF + wave_u * 64 * 16;
     if (t0 + C::BN <= Sk) {
-      const char* tile = kbase + (size_t)t0 * C::KROW;
+      const char* tile = k_tile(t);
 #pragma unroll
       for (int i = 0; i < C::KCHUNKS; ++i)
         if (k_live(i)) lds_copy16(tile, k_src[i], dst + i * C::THREADS * 16);
     } else {
+      // rows past the window's last key repeat it (>= t0: the same tile, and page)
+      const char* tile = PAGED ? k_tile(t) : kbase;
+      const int r0 = PAGED ? t0 : 0;
 #pragma unroll
       for (int i = 0; i < C::KCHUNKS; ++i) {
         const int gr = min(t0 + k_pos_row(i), Sk - 1);
-        if (k_live(i)) lds_copy16(kbase + (size_t)gr * C::KROW + k_pos_off(i), dst + i * C::THREADS * 16);
+        if (k_live(i)) lds_copy16(tile + (size_t)(gr - r0) * C::KROW + k_pos_off(i), dst + i * C::THREADS * 16);
       }
     }
   };
@@ -311,28 +356,30 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     const int t0 = t * C::BN;
     const uint32_t dst = v_lds + buf * C::VBUF + wave_u * 64 * 16;
     if (t0 + C::BN <= Sk) {
-      const char* tile = vbase + (size_t)t0 * C::VROW;
+      const char* tile = v_tile(t);
 #pragma unroll
       for (int i = 0; i < C::VCHUNKS; ++i)
         if (v_live(i)) lds_copy16(tile, v_src[i], dst + i * C::THREADS * 16);
     } else {
+      const char* tile = PAGED ? v_tile(t) : vbase;
+      const int r0 = PAGED ? t0 : 0;
 #pragma unroll
       for (int i = 0; i < C::VCHUNKS; ++i) {
         const int gr = min(t0 + v_pos_row(i), Sk - 1);
-        if (v_live(i)) lds_copy16(vbase + (size_t)gr * C::VROW + v_pos_off(i), dst + i * C::THREADS * 16);
+        if (v_live(i)) lds_copy16(tile + (size_t)(gr - r0) * C::VROW + v_pos_off(i), dst + i * C::THREADS * 16);
       }
     }
   };
   // the copies of full tiles, for iterations that only see full tiles (no branch)
   auto fill_k_full = [&](int t, int buf) {
-    const char* tile = kbase + (size_t)(t * C::BN) * C::KROW;
+    const char* tile = k_tile(t);
     const uint32_t dst = k_lds + buf * C::KBUF + wave_u * 64 * 16;
 #pragma unroll
     for (int i = 0; i < C::KCHUNKS; ++i)
       if (k_live(i)) lds_copy16(tile, k_src[i], dst + i * C::THREADS * 16);
   };
   auto fill_v_full = [&](int t, int buf) {
-    const char* tile = vbase + (size_t)(t * C::BN) * C::VROW;
+    const char* tile = v_tile(t);
     const uint32_t dst = v_lds + buf * C::VBUF + wave_u * 64 * 16;
 #pragma unroll
     for (int i = 0; i < C::VCHUNKS; ++i)
@@ -443,7 +490,10 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   __syncthreads();
   mask(sa, 0);
   float c_cur = c_q;
-  if constexpr (FP8) c_cur *= kscale[min(k_begin >> p.scale_shift, p.nbk - 1)];
+  if constexpr (FP8) {
+    if constexpr (PAGED) c_cur *= p.k_scale[page_row0(0) >> p.scale_shift];
+    else c_cur *= kscale[min(k_begin >> p.scale_shift, p.nbk - 1)];
+  }
   // tile 0 holds the window's key 0, which every row at a position >= 0 sees: finite there
   float xmax0 = rowmax(sa) * c_cur;
   float m_ref = xmax0 > -INFINITY ? ceilf(xmax0) : kRefEmpty;
@@ -486,9 +536,19 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     };
     // K and V scales of tile t+1 while iteration t runs; the loads for tile t+2 are
     // issued at the top of iteration t, ahead of the tile fills whose wait covers them
+    // K and V scales of a tile (PAGED: page scale blocks, indexed by the tile's cache row; a
+    // page holds whole scale blocks)
     auto sidx = [&](int tile) { return min((k_begin + tile * C::BN) >> p.scale_shift, p.nbk - 1); };
-    float ks_next = kscale[sidx(1)];
-    float vs_next = vscale[sidx(1)];
+    auto ksc = [&](int tile) {
+      if constexpr (PAGED) return p.k_scale[page_row0(tile) >> p.scale_shift];
+      else return kscale[sidx(tile)];
+    };
+    auto vsc = [&](int tile) {
+      if constexpr (PAGED) return p.v_scale[page_row0(tile) >> p.scale_shift];
+      else return vscale[sidx(tile)];
+    };
+    float ks_next = ksc(1);
+    float vs_next = vsc(1);
     // scale exponent e of a block whose row maximum is xmax (base 2): p = 2^(s c - m_ref - e)
     // puts the maximum in [2^kPHeadroom, 2^(kPHeadroom + 1)); 2^-e is the E8M0 scale code
     // 127 + e, kept >= 1 (a block more than 119 binades below the reference holds weights
@@ -499,7 +559,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
 
     float rv_cur;
     int sv_cur;
-    vsplit(vscale[sidx(0)], rv_cur, sv_cur);
+    vsplit(vsc(0), rv_cur, sv_cur);
     int eb_cur = block_exp(xmax0);
 
     v8i pa = v8i{0}, pb = v8i{0};
@@ -594,8 +654,8 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     auto step = [&](int t, v16f (&s_cur)[2], v16f (&s_next)[2], v8i& p_prev, v8i& p_cur) {
       const bool has_next = t + 1 < n;
       fix_units();
-      const float ks_pf = kscale[sidx(t + 2)];
-      const float vs_pf = vscale[sidx(t + 2)];
+      const float ks_pf = ksc(t + 2);
+      const float vs_pf = vsc(t + 2);
       if (t + 2 < n) fill_k(t + 2, (t + 2) % C::NBUF);
       if (has_next) qk((t + 1) % C::NBUF, s_next);
       pv(p_prev, sp_prev, sv_prev, (t + C::NBUF - 1) % C::NBUF);
@@ -673,8 +733,8 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
           }
         }
       };
-      const float ks_pf = kscale[sidx(t + 2)];
-      const float vs_pf = vscale[sidx(t + 2)];
+      const float ks_pf = ksc(t + 2);
+      const float vs_pf = vsc(t + 2);
       read_op(0, op[0]);
       read_op(1, op[1]);
       if constexpr (MASKED) {
@@ -988,7 +1048,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   }
 }
 
-template <bool FP8, int DQK, bool LEAN = false>
+template <bool FP8, int DQK, bool LEAN = false, bool PAGED = false>
 static hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   using C = Cfg<FP8, DQK>;
   AttnParams p;
@@ -1013,19 +1073,30 @@ static hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   p.nbk = FP8 ? (a.Skv + a.scale_block - 1) / a.scale_block : 0;
   p.cu_seqlens = a.cu_seqlens;
   p.max_seqlen = a.max_seqlen;
+  p.block_table = a.block_table;
+  p.kv_lens = a.kv_lens;
+  p.max_pages = a.max_pages;
+  p.num_pages = a.num_pages;
+  p.page_shift = a.page_size == 64 ? 6 : a.page_size == 128 ? 7 : 8;
   p.n_qtiles = ((a.cu_seqlens != nullptr ? a.max_seqlen : a.Sq) + C::BM - 1) / C::BM;
   p.scale_log2 = a.softmax_scale * kLog2e;
   const long long grid = (long long)p.n_qtiles * a.B * a.Hq;
-  hipLaunchKernelGGL((attn_fwd_kernel<FP8, DQK, LEAN>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<FP8, DQK, LEAN, PAGED>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd_fp8(const AttnArgs& a, bool lean, hipStream_t stream) {
+  if (a.block_table != nullptr) {
+    if (lean) return a.Dqk == 192 ? launch<true, 192, true, true>(a, stream) : launch<true, 128, true, true>(a, stream);
+    return a.Dqk == 192 ? launch<true, 192, false, true>(a, stream) : launch<true, 128, false, true>(a, stream);
+  }
   if (lean) return a.Dqk == 192 ? launch<true, 192, true>(a, stream) : launch<true, 128, true>(a, stream);
   return a.Dqk == 192 ? launch<true, 192>(a, stream) : launch<true, 128>(a, stream);
 }
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream) {
+  if (a.block_table != nullptr)
+    return a.Dqk == 192 ? launch<false, 192, false, true>(a, stream) : launch<false, 128, false, true>(a, stream);
   return a.Dqk == 192 ? launch<false, 192>(a, stream) : launch<false, 128>(a, stream);
 }
 

@@ -227,6 +227,88 @@ zyfa_status zyfa_attn_fwd_bf16_varlen(const uint16_t* q, const uint16_t* k, cons
   return ok();
 }
 
+static zyfa_status check_paged(const void* k_cache, const void* v_cache, const int* kv_lens,
+                               const int* block_table, int n_seqs, int max_pages, int num_pages, int page_size, int Hkv,
+                               int Dqk, int Dv) {
+  if (!kv_lens || !block_table) return fail(ZYFA_ERR_INVALID_ARGUMENT, "kv_lens and block_table must be non-null");
+  if (((uintptr_t)kv_lens & 3u) != 0 || ((uintptr_t)block_table & 3u) != 0)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "kv_lens and block_table must be 4-byte aligned");
+  if (page_size != 64 && page_size != 128 && page_size != 256)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "page_size must be 64, 128 or 256 (got %d)", page_size);
+  if (max_pages <= 0 || num_pages <= 0)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "max_pages and num_pages must be positive (got %d, %d)", max_pages,
+                num_pages);
+  if ((long long)max_pages * page_size > kMaxPosition)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "max_pages * page_size must be at most 2^30");
+  const long long dmax = Dqk > Dv ? Dqk : Dv;
+  if ((long long)num_pages * Hkv * page_size * dmax > kMaxElems ||
+      (long long)n_seqs * max_pages > 0x7FFFFFFFLL)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "tensor too large");
+  if (k_cache == v_cache) return fail(ZYFA_ERR_INVALID_ARGUMENT, "k_cache and v_cache must be distinct");
+  return ZYFA_OK;
+}
+
+zyfa_status zyfa_attn_fwd_fp8_paged(const uint8_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                    const float* q_scale, const float* k_cache_scale, const float* v_cache_scale,
+                                    int scale_block, uint16_t* o, float* lse, const int* cu_seqlens,
+                                    const int* kv_lens, const int* block_table, int n_seqs, int max_seqlen,
+                                    int max_pages, int num_pages, int page_size, int Hq, int Hkv, int T, int Dqk,
+                                    int Dv, float softmax_scale, int lean, void* stream) {
+  if (lean != 0 && lean != 1) return fail(ZYFA_ERR_INVALID_ARGUMENT, "lean must be 0 or 1");
+  zyfa_status st = check_attn_common(q, k_cache, v_cache, o, lse, 1, Hq, Hkv, T, T, 0, 0, T, Dqk, Dv, softmax_scale);
+  if (st != ZYFA_OK) return st;
+  st = check_varlen(cu_seqlens, n_seqs, max_seqlen, Hq, T);
+  if (st != ZYFA_OK) return st;
+  st = check_paged(k_cache, v_cache, kv_lens, block_table, n_seqs, max_pages, num_pages, page_size, Hkv, Dqk, Dv);
+  if (st != ZYFA_OK) return st;
+  if (!q_scale || !k_cache_scale || !v_cache_scale)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "scale pointers must be non-null");
+  if (!aligned16(q_scale) || !aligned16(k_cache_scale) || !aligned16(v_cache_scale))
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  if (scale_block != 64 && scale_block != 128)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "scale_block must be 64 or 128 (got %d)", scale_block);
+  if (page_size % scale_block != 0)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "page_size (%d) must be a multiple of scale_block (%d)", page_size,
+                scale_block);
+  zyfa::AttnArgs a{q,  k_cache, v_cache, q_scale, k_cache_scale, v_cache_scale, o, lse, n_seqs, Hq, Hkv,
+                   T,  T,       0,       0,       T,             Dqk,                       Dv, scale_block, softmax_scale};
+  a.cu_seqlens = cu_seqlens;
+  a.max_seqlen = max_seqlen;
+  a.block_table = block_table;
+  a.kv_lens = kv_lens;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.page_size = page_size;
+  hipError_t e = zyfa::launch_attn_fwd_fp8(a, lean == 1, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ZYFA_ERR_LAUNCH, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+zyfa_status zyfa_attn_fwd_bf16_paged(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                     uint16_t* o, float* lse, const int* cu_seqlens, const int* kv_lens,
+                                     const int* block_table, int n_seqs, int max_seqlen, int max_pages,
+                                     int num_pages, int page_size, int Hq, int Hkv, int T, int Dqk, int Dv,
+                                     float softmax_scale, void* stream) {
+  zyfa_status st = check_attn_common(q, k_cache, v_cache, o, lse, 1, Hq, Hkv, T, T, 0, 0, T, Dqk, Dv, softmax_scale);
+  if (st != ZYFA_OK) return st;
+  st = check_varlen(cu_seqlens, n_seqs, max_seqlen, Hq, T);
+  if (st != ZYFA_OK) return st;
+  st = check_paged(k_cache, v_cache, kv_lens, block_table, n_seqs, max_pages, num_pages, page_size, Hkv, Dqk, Dv);
+  if (st != ZYFA_OK) return st;
+  zyfa::AttnArgs a{q, k_cache, v_cache, nullptr, nullptr, nullptr, o,  lse, n_seqs, Hq, Hkv,
+                   T, T,       0,       0,       T,       Dqk,     Dv, 0,   softmax_scale};
+  a.cu_seqlens = cu_seqlens;
+  a.max_seqlen = max_seqlen;
+  a.block_table = block_table;
+  a.kv_lens = kv_lens;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.page_size = page_size;
+  hipError_t e = zyfa::launch_attn_fwd_bf16(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ZYFA_ERR_LAUNCH, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 zyfa_status zyfa_attn_merge(const uint16_t* o_parts, const float* lse_parts, int n_parts, uint16_t* o, float* lse,
                             long long rows, int Dv, void* stream) {
   if (!o_parts || !lse_parts || !o) return fail(ZYFA_ERR_INVALID_ARGUMENT, "o_parts, lse_parts and o must be non-null");

@@ -27,6 +27,11 @@ struct AttnArgs {
   // being tokens cu_seqlens[b] .. cu_seqlens[b+1] - 1 (device array of B + 1 ints)
   const int* cu_seqlens = nullptr;
   int max_seqlen = 0;
+  // paged key/value cache (non-null block_table): K, V [num_pages, Hkv, page_size, D];
+  // sequence b's pages block_table[b * max_pages ...], its token count kv_lens[b]
+  const int* block_table = nullptr;
+  const int* kv_lens = nullptr;
+  int max_pages = 0, num_pages = 0, page_size = 0;
 };
 
 // keys per tile of the attention kernels: a key window must start on a tile boundary

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define ZYFA_ABI_VERSION 3
+#define ZYFA_ABI_VERSION 4
 
 typedef enum zyfa_status {
   ZYFA_OK = 0,
@@ -248,6 +248,57 @@ zyfa_status zyfa_attn_fwd_fp8_varlen(const uint8_t* q, const uint8_t* k, const u
 zyfa_status zyfa_attn_fwd_bf16_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                                       float* lse, const int* cu_seqlens, int n_seqs, int max_seqlen, int Hq, int Hkv,
                                       int T, int Dqk, int Dv, float softmax_scale, void* stream);
+
+/*
+ * zyfa_attn_fwd_fp8_paged / zyfa_attn_fwd_bf16_paged -- prefill of chunks of new tokens
+ * against a paged key/value cache.
+ *
+ * Source: ZYFA page, "Future Work" (paged KV caches, variable-length batches). Sequence i
+ * holds kv_lens[i] tokens whose keys and values sit in pages of a shared cache; its
+ * chunk of L_i = cu_seqlens[i+1] - cu_seqlens[i] new tokens is the last L_i of them (their
+ * keys and values already written into the cache). Row r of the chunk is the token at
+ * position kv_lens[i] - L_i + r and sees the sequence's keys 0 .. kv_lens[i] - L_i + r:
+ * zyfa_attn_fwd_fp8_range on the gathered keys with q_offset = kv_lens[i] - L_i.
+ *
+ *   q            [Hq, T, Dqk]: the chunks packed along the token axis as in
+ *                zyfa_attn_fwd_fp8_varlen (cu_seqlens: starts on multiples of 64;
+ *                max_seqlen). A chunk padded at its end to a multiple of 64 rows counts
+ *                its padding as the sequence's last tokens (in kv_lens[i], with keys and
+ *                values in the cache after the sequence's own): the causal rule keeps them
+ *                out of the real rows' results.
+ *   k_cache      [num_pages, Hkv, page_size, Dqk]; v_cache [num_pages, Hkv, page_size, Dv]:
+ *                page p holds page_size consecutive tokens of every key/value head.
+ *   k_cache_scale, v_cache_scale  FP8: [num_pages, Hkv, page_size / scale_block], the
+ *                layout zyfa_quantize_fp8 writes for the cache viewed as
+ *                B = num_pages, H = Hkv, S = page_size. page_size must be a multiple of
+ *                scale_block.
+ *   q_scale      FP8: [Hq, ceil(T / scale_block)], as in zyfa_attn_fwd_fp8_varlen.
+ *   block_table  device int32 [n_seqs, max_pages]: logical page j of sequence i (its tokens
+ *                j * page_size ..) is cache page block_table[i * max_pages + j]. Pages may
+ *                be shared between sequences and appear in any order.
+ *   kv_lens      device int32 [n_seqs]: L_i <= kv_lens[i] <= max_pages * page_size.
+ *   page_size    64, 128 or 256.
+ *   o, lse       out: [Hq, T, Dv] bfloat16 and (may be NULL) [Hq, T] float32; rows outside
+ *                every chunk are not written.
+ *
+ * The device arrays are read on the device: a sequence whose cu_seqlens or kv_lens entries
+ * break the rules is left unwritten (no error is reported); a block_table entry outside
+ * [0, num_pages) is clamped into it (the sequence's result is then meaningless, but no
+ * read leaves the cache). Other rules (pointers, alignment, streams, errors, head shapes,
+ * lean) as zyfa_attn_fwd_fp8_varlen.
+ */
+zyfa_status zyfa_attn_fwd_fp8_paged(const uint8_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                    const float* q_scale, const float* k_cache_scale, const float* v_cache_scale,
+                                    int scale_block, uint16_t* o, float* lse, const int* cu_seqlens,
+                                    const int* kv_lens, const int* block_table, int n_seqs, int max_seqlen,
+                                    int max_pages, int num_pages, int page_size, int Hq, int Hkv, int T, int Dqk,
+                                    int Dv, float softmax_scale, int lean, void* stream);
+
+zyfa_status zyfa_attn_fwd_bf16_paged(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                     uint16_t* o, float* lse, const int* cu_seqlens, const int* kv_lens,
+                                     const int* block_table, int n_seqs, int max_seqlen, int max_pages,
+                                     int num_pages, int page_size, int Hq, int Hkv, int T, int Dqk, int Dv,
+                                     float softmax_scale, void* stream);
 
 /*
  * zyfa_attn_merge -- combine partial attention results over disjoint key sets.

@@ -38,14 +38,15 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"zyfa_abi_version", "zyfa_status_string", "zyfa_last_error", "zyfa_quantize_fp8",
                           "zyfa_attn_fwd_fp8", "zyfa_attn_fwd_fp8_lean", "zyfa_attn_fwd_bf16",
                           "zyfa_attn_fwd_fp8_range", "zyfa_attn_fwd_bf16_range", "zyfa_attn_merge",
-                          "zyfa_attn_fwd_fp8_varlen", "zyfa_attn_fwd_bf16_varlen"}
+                          "zyfa_attn_fwd_fp8_varlen", "zyfa_attn_fwd_bf16_varlen", "zyfa_attn_fwd_fp8_paged",
+                          "zyfa_attn_fwd_bf16_paged"}
     raw = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.zyfa_abi_version() == 3
+    assert lib.zyfa_abi_version() == 4
     assert lib.zyfa_status_string(0) == b"ZYFA_OK"
     assert lib.zyfa_status_string(1) == b"ZYFA_ERR_INVALID_ARGUMENT"
     assert lib.zyfa_status_string(2) == b"ZYFA_ERR_UNSUPPORTED"
@@ -149,6 +150,39 @@ def test_varlen_argument_checks(lib, kw, expect):
 @pytest.mark.parametrize("kw", [dict(qs=None), dict(blk=32), dict(lean=3)])
 def test_fp8_varlen_scale_and_mode_checks(lib, kw):
     assert fp8_varlen(lib, **kw) == INVALID
+
+
+def fp8_paged(lib, q=P, k=P2, v=P3, qs=P4, ks=P5, vs=P6, blk=128, o=P7, lse=None, cu=0x80000, kvl=0x90000,
+              bt=0xA0000, n=3, maxs=300, maxp=8, nump=30, page=128, Hq=4, Hkv=2, T=1000, Dqk=128, Dv=128,
+              scale=0.088, lean=0):
+    return lib.zyfa_attn_fwd_fp8_paged(q, k, v, qs, ks, vs, blk, o, lse, cu, kvl, bt, n, maxs, maxp, nump, page, Hq,
+                                       Hkv, T, Dqk, Dv, scale, lean, None)
+
+
+def bf16_paged(lib, q=P, k=P2, v=P3, o=P7, lse=None, cu=0x80000, kvl=0x90000, bt=0xA0000, n=3, maxs=300, maxp=8,
+               nump=30, page=128, Hq=4, Hkv=2, T=1000, Dqk=128, Dv=128, scale=0.088):
+    return lib.zyfa_attn_fwd_bf16_paged(q, k, v, o, lse, cu, kvl, bt, n, maxs, maxp, nump, page, Hq, Hkv, T, Dqk, Dv,
+                                        scale, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(o=MIS), INVALID), (dict(cu=None), INVALID),
+    (dict(kvl=None), INVALID), (dict(bt=None), INVALID), (dict(kvl=0x90002), INVALID), (dict(bt=0xA0001), INVALID),
+    (dict(n=0), INVALID), (dict(maxs=0), INVALID), (dict(maxs=1001), INVALID), (dict(maxp=0), INVALID),
+    (dict(nump=0), INVALID), (dict(page=32), INVALID), (dict(page=192), INVALID), (dict(page=512), INVALID),
+    (dict(maxp=1 << 23, page=256), INVALID), (dict(nump=1 << 30), INVALID), (dict(v=P2), INVALID),
+    (dict(Hq=6, Hkv=4), INVALID), (dict(scale=0.0), INVALID), (dict(Dqk=64, Dv=64), UNSUPPORTED),
+    (dict(o=P), INVALID),
+])
+def test_paged_argument_checks(lib, kw, expect):
+    assert bf16_paged(lib, **kw) == expect
+    assert lib.zyfa_last_error() != b""
+    assert fp8_paged(lib, **kw) == expect
+
+
+@pytest.mark.parametrize("kw", [dict(qs=None), dict(ks=MIS), dict(blk=32), dict(lean=2), dict(page=64, blk=128)])
+def test_fp8_paged_scale_and_mode_checks(lib, kw):
+    assert fp8_paged(lib, **kw) == INVALID
 
 
 def merge(lib, op=P, lp=P2, n=2, o=P3, lse=None, rows=1000, Dv=128):

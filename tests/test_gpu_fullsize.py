@@ -193,3 +193,52 @@ def test_full_size_varlen_batch():
         ref_heads.append(ro[0])
         got_heads.append(bf16_from_f64(o[hq, torch.from_numpy(rows).to(dev)]))
     _check("gqa32k varlen", got_heads, ref_heads, rows_e, rows_l, BARS["fp8"])
+
+
+def test_full_size_paged_prefill():
+    """The paged measurements of the benchmark: the 32K GQA keys and values in a shuffled
+    cache of 128-token pages (FP8 exact), the whole sequence as one chunk and its second
+    half as a chunk after a 16K cached prefix. Bit for bit against the plain and range calls
+    on the contiguous tensors, and on sampled rows of two heads against the oracle on the
+    pages it gathers through the block table."""
+    from oracle import gather_pages, window_attention
+    import bench
+    w = WORKLOADS["gqa32k"]
+    print("case: gqa32k paged prefill", flush=True)
+    q, k, v = generate(w, seed=0)
+    dev = "cuda"
+    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    del q, k, v
+    blk, S = w.scale_block, w.S
+    qc, qs = zy.quantize_fp8(qd, blk)
+    kc, ks = zy.quantize_fp8(kd, blk)
+    vc, vs = zy.quantize_fp8(vd, blk)
+    del qd, kd, vd
+    kp, vp, ksp, vsp, bt = bench.paged_cache(w, kc, vc, ks, vs, torch)
+    kvl = torch.tensor([S], dtype=torch.int32, device=dev)
+    half = S // 2
+    o_w, l_w = zy.attn_fwd_fp8_paged(qc[0], kp, vp, qs[0], ksp, vsp, blk, torch.tensor([0, S], dtype=torch.int32,
+                                     device=dev), kvl, bt, S, w.softmax_scale, return_lse=True)
+    o_c, l_c = zy.attn_fwd_fp8_paged(qc[0, :, half:].contiguous(), kp, vp, qs[0, :, half // blk:].contiguous(), ksp,
+                                     vsp, blk, torch.tensor([0, S - half], dtype=torch.int32, device=dev), kvl, bt,
+                                     S - half, w.softmax_scale, return_lse=True)
+    o_full, l_full = zy.attn_fwd_fp8(qc, kc, vc, qs, ks, vs, blk, w.softmax_scale, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_w, o_full[0]) and torch.equal(l_w, l_full[0])
+    assert torch.equal(o_c, o_full[0, :, half:]) and torch.equal(l_c, l_full[0, :, half:])
+    del o_full, l_full
+    rows_e = np.arange(256)
+    rows_l = _late_rows(S - half, seed=5)
+    rows = np.concatenate([rows_e, rows_l])
+    table = bt[0].cpu().numpy()
+    group = w.Hq // w.Hkv
+    ref_heads, got_heads = [], []
+    for hq in (0, w.Hq - 1):
+        hk = hq // group
+        qq = dequantize_blocks(qc[0:1, hq:hq + 1].cpu().numpy(), qs[0:1, hq:hq + 1].cpu().numpy(), blk)
+        kk, vv = (gather_pages(dequantize_blocks(c[:, hk:hk + 1].cpu().numpy(), s[:, hk:hk + 1].cpu().numpy(), blk),
+                               table, S) for c, s in ((kp, ksp), (vp, vsp)))
+        ro, _ = window_attention(qq[:, :, half:], kk[None], vv[None], w.softmax_scale, q_offset=half, rows=rows)
+        ref_heads.append(ro[0, 0])
+        got_heads.append(bf16_from_f64(o_c[hq, torch.from_numpy(rows).to(dev)]))
+    _check("gqa32k paged chunk", got_heads, ref_heads, rows_e, rows_l, BARS["fp8"])

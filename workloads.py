@@ -109,3 +109,28 @@ def sample_rows(S: int, n: int, seed: int = 0):
     fixed = [0, 1, S // 2, S - 1]
     extra = rng.choice(S, size=max(0, min(n, S) - len(fixed)), replace=False)
     return np.unique(np.concatenate([np.array(fixed), extra]).clip(0, S - 1))
+
+
+def page_table(kv_lens, page_size: int, seed: int = 0, spare: int = 3):
+    """A shuffled layout of a paged key/value cache: sequence i needs
+    ceil(kv_lens[i] / page_size) pages, taken in a seeded random order from a cache of
+    that many pages plus `spare` unused ones. Returns (block_table int32 [n, max_pages],
+    num_pages); table entries past a sequence's pages hold -1."""
+    need = [-(-int(n) // page_size) for n in kv_lens]
+    num_pages = sum(need) + spare
+    perm = np.random.default_rng([777, page_size, seed]).permutation(num_pages)
+    table = np.full((len(need), max(1, max(need))), -1, dtype=np.int32)
+    at = 0
+    for i, m in enumerate(need):
+        table[i, :m] = perm[at:at + m]
+        at += m
+    return table, num_pages
+
+
+def scatter_pages(cache, table_row, x):
+    """Write x [H, n, D] (one sequence's tokens) into cache [pages, H, P, D] at the pages
+    table_row lists, in order (data placement only)."""
+    P = cache.shape[2]
+    for j in range(-(-x.shape[1] // P)):
+        part = x[:, j * P:(j + 1) * P]
+        cache[int(table_row[j]), :, :part.shape[1]] = part
