@@ -261,15 +261,30 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   const char* vbase = p.v + (kv_row0 + k_begin) * C::VROW;
   const float* kscale = p.k_scale + kv_sc0;
   const float* vscale = p.v_scale + kv_sc0;
-  // PAGED: the row of the cache ([pages x Hkv x page rows] rows of D) holding key tile t's
-  // first key; a tile never straddles pages (a page holds whole tiles). Page indices are
-  // clamped to the table and the cache, so a malformed table reads wrong rows, never past
-  // the tensors.
-  auto page_row0 = [&](int t) -> size_t {
-    const int pos = t * C::BN;
-    const int j = min(pos >> p.page_shift, p.max_pages - 1);
-    const int page = min(max(p.block_table[(size_t)b * p.max_pages + j], 0), p.num_pages - 1);
-    return (((size_t)page * p.Hkv + hkv) << p.page_shift) + (pos & ((1 << p.page_shift) - 1));
+  // PAGED: the cache page holding key tile t (a tile never straddles pages: a page holds
+  // whole tiles), and the row of the cache ([pages x Hkv x page rows] rows of D) holding
+  // the tile's first key. Page indices are clamped to the table and the cache, so a
+  // malformed table reads wrong rows, never past the tensors.
+  auto page_of = [&](int t) -> int {
+    const int j = min((t * C::BN) >> p.page_shift, p.max_pages - 1);
+    return min(max(p.block_table[(size_t)b * p.max_pages + j], 0), p.num_pages - 1);
+  };
+  auto page_row = [&](int pg, int t) -> size_t {
+    return (((size_t)pg * p.Hkv + hkv) << p.page_shift) + ((t * C::BN) & ((1 << p.page_shift) - 1));
+  };
+  // the pages of tiles t+1 and t+2 while iteration t runs: the page of tile t+3 is read
+  // during iteration t (like the FP8 scales), so that no copy waits for the table
+  int pg1 = 0, pg2 = 0;
+  const int pg0 = PAGED ? page_of(0) : 0;
+  if constexpr (PAGED) {
+    pg1 = page_of(1);
+    pg2 = page_of(2);
+  }
+  auto next_pages = [&](int pg3) {
+    if constexpr (PAGED) {
+      pg1 = pg2;
+      pg2 = pg3;
+    }
   };
 
   // ---- Q operand (B of S^T = K Q^T): lane holds Q[my_q][c*KSTEP + h*KSTEP/2 ...] ----
@@ -324,26 +339,26 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   for (int i = 0; i < C::VCHUNKS; ++i) v_src[i] = v_pos_row(i) * C::VROW + v_pos_off(i);
   const uint32_t k_lds = lds_address(kring), v_lds = lds_address(vring);
 
-  // first K / V byte of key tile t (t0 = t * BN)
-  auto k_tile = [&](int t) -> const char* {
-    if constexpr (PAGED) return p.k + page_row0(t) * C::KROW;
+  // first K / V byte of key tile t (t0 = t * BN; PAGED: in cache page pg)
+  auto k_tile = [&](int t, int pg) -> const char* {
+    if constexpr (PAGED) return p.k + page_row(pg, t) * C::KROW;
     else return kbase + (size_t)(t * C::BN) * C::KROW;
   };
-  auto v_tile = [&](int t) -> const char* {
-    if constexpr (PAGED) return p.v + page_row0(t) * C::VROW;
+  auto v_tile = [&](int t, int pg) -> const char* {
+    if constexpr (PAGED) return p.v + page_row(pg, t) * C::VROW;
     else return vbase + (size_t)(t * C::BN) * C::VROW;
   };
-  auto fill_k = [&](int t, int buf) {
+  auto fill_k = [&](int t, int buf, int pg) {
     const int t0 = t * C::BN;
     const uint32_t dst = k_lds + buf * C::KBUF + wave_u * 64 * 16;
     if (t0 + C::BN <= Sk) {
-      const char* tile = k_tile(t);
+      const char* tile = k_tile(t, pg);
 #pragma unroll
       for (int i = 0; i < C::KCHUNKS; ++i)
         if (k_live(i)) lds_copy16(tile, k_src[i], dst + i * C::THREADS * 16);
     } else {
       // rows past the window's last key repeat it (>= t0: the same tile, and page)
-      const char* tile = PAGED ? k_tile(t) : kbase;
+      const char* tile = PAGED ? k_tile(t, pg) : kbase;
       const int r0 = PAGED ? t0 : 0;
 #pragma unroll
       for (int i = 0; i < C::KCHUNKS; ++i) {
@@ -352,16 +367,16 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       }
     }
   };
-  auto fill_v = [&](int t, int buf) {
+  auto fill_v = [&](int t, int buf, int pg) {
     const int t0 = t * C::BN;
     const uint32_t dst = v_lds + buf * C::VBUF + wave_u * 64 * 16;
     if (t0 + C::BN <= Sk) {
-      const char* tile = v_tile(t);
+      const char* tile = v_tile(t, pg);
 #pragma unroll
       for (int i = 0; i < C::VCHUNKS; ++i)
         if (v_live(i)) lds_copy16(tile, v_src[i], dst + i * C::THREADS * 16);
     } else {
-      const char* tile = PAGED ? v_tile(t) : vbase;
+      const char* tile = PAGED ? v_tile(t, pg) : vbase;
       const int r0 = PAGED ? t0 : 0;
 #pragma unroll
       for (int i = 0; i < C::VCHUNKS; ++i) {
@@ -371,15 +386,15 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     }
   };
   // the copies of full tiles, for iterations that only see full tiles (no branch)
-  auto fill_k_full = [&](int t, int buf) {
-    const char* tile = k_tile(t);
+  auto fill_k_full = [&](int t, int buf, int pg) {
+    const char* tile = k_tile(t, pg);
     const uint32_t dst = k_lds + buf * C::KBUF + wave_u * 64 * 16;
 #pragma unroll
     for (int i = 0; i < C::KCHUNKS; ++i)
       if (k_live(i)) lds_copy16(tile, k_src[i], dst + i * C::THREADS * 16);
   };
-  auto fill_v_full = [&](int t, int buf) {
-    const char* tile = v_tile(t);
+  auto fill_v_full = [&](int t, int buf, int pg) {
+    const char* tile = v_tile(t, pg);
     const uint32_t dst = v_lds + buf * C::VBUF + wave_u * 64 * 16;
 #pragma unroll
     for (int i = 0; i < C::VCHUNKS; ++i)
@@ -462,9 +477,9 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   for (int d = 0; d < 4; ++d) oacc[d] = v16f{0};
 
   // ---- prologue: K0, V0, K1 resident; scores and maxima of tile 0 ----
-  fill_k(0, 0);
-  fill_v(0, 0);
-  if (n > 1) fill_k(1, 1);
+  fill_k(0, 0, pg0);
+  fill_v(0, 0, pg0);
+  if (n > 1) fill_k(1, 1, pg1);
   {
     // the PV stage of the first iteration multiplies an all-zero P with the buffer of
     // "V_-1": make that buffer finite
@@ -491,7 +506,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   mask(sa, 0);
   float c_cur = c_q;
   if constexpr (FP8) {
-    if constexpr (PAGED) c_cur *= p.k_scale[page_row0(0) >> p.scale_shift];
+    if constexpr (PAGED) c_cur *= p.k_scale[page_row(pg0, 0) >> p.scale_shift];
     else c_cur *= kscale[min(k_begin >> p.scale_shift, p.nbk - 1)];
   }
   // tile 0 holds the window's key 0, which every row at a position >= 0 sees: finite there
@@ -539,16 +554,16 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     // K and V scales of a tile (PAGED: page scale blocks, indexed by the tile's cache row; a
     // page holds whole scale blocks)
     auto sidx = [&](int tile) { return min((k_begin + tile * C::BN) >> p.scale_shift, p.nbk - 1); };
-    auto ksc = [&](int tile) {
-      if constexpr (PAGED) return p.k_scale[page_row0(tile) >> p.scale_shift];
+    auto ksc = [&](int tile, int pg) {
+      if constexpr (PAGED) return p.k_scale[page_row(pg, tile) >> p.scale_shift];
       else return kscale[sidx(tile)];
     };
-    auto vsc = [&](int tile) {
-      if constexpr (PAGED) return p.v_scale[page_row0(tile) >> p.scale_shift];
+    auto vsc = [&](int tile, int pg) {
+      if constexpr (PAGED) return p.v_scale[page_row(pg, tile) >> p.scale_shift];
       else return vscale[sidx(tile)];
     };
-    float ks_next = ksc(1);
-    float vs_next = vsc(1);
+    float ks_next = ksc(1, pg1);
+    float vs_next = vsc(1, pg1);
     // scale exponent e of a block whose row maximum is xmax (base 2): p = 2^(s c - m_ref - e)
     // puts the maximum in [2^kPHeadroom, 2^(kPHeadroom + 1)); 2^-e is the E8M0 scale code
     // 127 + e, kept >= 1 (a block more than 119 binades below the reference holds weights
@@ -559,7 +574,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
 
     float rv_cur;
     int sv_cur;
-    vsplit(vsc(0), rv_cur, sv_cur);
+    vsplit(vsc(0, pg0), rv_cur, sv_cur);
     int eb_cur = block_exp(xmax0);
 
     v8i pa = v8i{0}, pb = v8i{0};
@@ -654,9 +669,10 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     auto step = [&](int t, v16f (&s_cur)[2], v16f (&s_next)[2], v8i& p_prev, v8i& p_cur) {
       const bool has_next = t + 1 < n;
       fix_units();
-      const float ks_pf = ksc(t + 2);
-      const float vs_pf = vsc(t + 2);
-      if (t + 2 < n) fill_k(t + 2, (t + 2) % C::NBUF);
+      const int pg3 = PAGED ? page_of(t + 3) : 0;
+      const float ks_pf = ksc(t + 2, pg2);
+      const float vs_pf = vsc(t + 2, pg2);
+      if (t + 2 < n) fill_k(t + 2, (t + 2) % C::NBUF, pg2);
       if (has_next) qk((t + 1) % C::NBUF, s_next);
       pv(p_prev, sp_prev, sv_prev, (t + C::NBUF - 1) % C::NBUF);
 
@@ -694,7 +710,8 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       ks_next = ks_pf;
       vs_next = vs_pf;
       __syncthreads();
-      if (has_next) fill_v(t + 1, (t + 1) % C::NBUF);
+      if (has_next) fill_v(t + 1, (t + 1) % C::NBUF, pg1);
+      next_pages(pg3);
     };
 
     // Steady iteration, hand-ordered: slot i issues matrix instruction i (QK of tile t+1,
@@ -733,14 +750,15 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
           }
         }
       };
-      const float ks_pf = ksc(t + 2);
-      const float vs_pf = vsc(t + 2);
+      const int pg3 = PAGED ? page_of(t + 3) : 0;
+      const float ks_pf = ksc(t + 2, pg2);
+      const float vs_pf = vsc(t + 2, pg2);
       read_op(0, op[0]);
       read_op(1, op[1]);
       if constexpr (MASKED) {
-        if (t + 2 < n) fill_k(t + 2, (t + 2) % C::NBUF);
+        if (t + 2 < n) fill_k(t + 2, (t + 2) % C::NBUF, pg2);
       } else {
-        fill_k_full(t + 2, (t + 2) % C::NBUF);
+        fill_k_full(t + 2, (t + 2) % C::NBUF, pg2);
       }
       s_next[0] = v16f{0};
       s_next[1] = v16f{0};
@@ -808,10 +826,11 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       __syncthreads();
       // V_{t+1} replaces V_{t-1}, last read by this iteration's PV products
       if constexpr (MASKED) {
-        fill_v(t + 1, (t + 1) % C::NBUF);
+        fill_v(t + 1, (t + 1) % C::NBUF, pg1);
       } else {
-        fill_v_full(t + 1, (t + 1) % C::NBUF);
+        fill_v_full(t + 1, (t + 1) % C::NBUF, pg1);
       }
+      next_pages(pg3);
     };
 
     int t = 0;
@@ -895,7 +914,8 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     // Generic iteration (the diagonal tiles and the tail), in program order.
     auto step = [&](int t) {
       fix_o();
-      if (t + 2 < n) fill_k(t + 2, t & 1);
+      const int pg3 = PAGED ? page_of(t + 3) : 0;
+      if (t + 2 < n) fill_k(t + 2, t & 1, pg2);
       {
         const char* vb = vring + ((t + 1) & 1) * C::VBUF + v_off0;  // V of tile t-1
 #pragma unroll
@@ -914,7 +934,8 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       if (t + 1 < n) qk((t + 1) & 1, sc);
       wait_fills();
       __syncthreads();
-      if (t + 1 < n) fill_v(t + 1, (t + 1) & 1);
+      if (t + 1 < n) fill_v(t + 1, (t + 1) & 1, pg1);
+      next_pages(pg3);
     };
 
     // Steady iteration, hand-ordered: slot i issues matrix instruction i (PV of tile t-1:
@@ -940,10 +961,11 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     auto steady_step = [&](auto masked_tag, int t) {
       constexpr bool MASKED = decltype(masked_tag)::value;
       fix_o();
+      const int pg3 = PAGED ? page_of(t + 3) : 0;
       if constexpr (MASKED) {
-        if (t + 2 < n) fill_k(t + 2, t & 1);
+        if (t + 2 < n) fill_k(t + 2, t & 1, pg2);
       } else {
-        fill_k_full(t + 2, t & 1);
+        fill_k_full(t + 2, t & 1, pg2);
       }
       const char* kb = kring + ((t + 1) & 1) * C::KBUF;           // K of tile t+1
       const char* vb = vring + ((t + 1) & 1) * C::VBUF + v_off0;  // V of tile t-1
@@ -1016,10 +1038,11 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       __syncthreads();
       // V_{t+1} replaces V_{t-1}, last read by this iteration's PV products
       if constexpr (MASKED) {
-        fill_v(t + 1, (t + 1) & 1);
+        fill_v(t + 1, (t + 1) & 1, pg1);
       } else {
-        fill_v_full(t + 1, (t + 1) & 1);
+        fill_v_full(t + 1, (t + 1) & 1, pg1);
       }
+      next_pages(pg3);
     };
 
     // the tile-0 scores are in sc (masked); the steady iterations need the maxima of
