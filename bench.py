@@ -342,6 +342,64 @@ def paged_prefill(w, qc, kc, vc, qs, ks, vs, steps, warmup, stream, torch, zy):
     return rec
 
 
+DECODE_BATCH = 8
+
+
+def decode_setup(w, kc, vc, ks, vs, torch, zy, seed=1):
+    """Decode inputs at the benchmark's heads: DECODE_BATCH sequences of S tokens each, every
+    one holding the benchmark's FP8 keys and values in its own PAGE_SIZE-token pages of one
+    shared cache (seeded random page order), and one new query per sequence and head
+    (seeded Gaussian, quantized with one scale per KV group). Returns (q codes [B, Hq, D],
+    q scales, k cache, v cache, k scales, v scales, kv_lens, block table)."""
+    from workloads import custom, generate, page_table
+    B, S, P, blk, dev = DECODE_BATCH, w.S, PAGE_SIZE, w.scale_block, kc.device
+    table, num_pages = page_table([S] * B, P, seed=seed)
+    bt = torch.from_numpy(table).to(dev)
+
+    def to_pages(x, rows):  # [1, H, S', ...] -> [num_pages, H, rows per page, ...], every sequence a copy
+        pages = x[0].reshape(x.shape[1], S // P, rows, *x.shape[3:]).transpose(0, 1)
+        cache = torch.zeros((num_pages, *pages.shape[1:]), dtype=x.dtype, device=dev)
+        for i in range(B):
+            cache[bt[i].long()] = pages
+        return cache
+
+    g = w.Hq // w.Hkv
+    q, _, _ = generate(custom(1, B, B, w.Hq, w.Dqk, w.Dv, wid=950), seed=seed)
+    qd = torch.from_numpy(q[0]).to(dev).reshape(B, w.Hkv, g, w.Dqk)
+    qc, qs = zy.quantize_fp8(qd, blk)
+    kvl = torch.full((B,), S, dtype=torch.int32, device=dev)
+    return (qc.reshape(B, w.Hq, w.Dqk), qs, to_pages(kc, P), to_pages(vc, P), to_pages(ks, P // blk),
+            to_pages(vs, P // blk), kvl, bt)
+
+
+def decode_batch(w, kc, vc, ks, vs, steps, warmup, stream, torch, zy):
+    """The decode entry point (FP8 exact) on decode_setup's batch: one call is the split
+    attention kernel plus the merge. HBM-bound: algorithmic bytes per call are the cached
+    keys and values (codes and scales) of every sequence, the queries, the partial results
+    (written and read once) and the output."""
+    if w.B != 1 or w.S % PAGE_SIZE != 0:
+        return None
+    qc, qs, kp, vp, ksp, vsp, kvl, bt = decode_setup(w, kc, vc, ks, vs, torch, zy)
+    B, S, blk = DECODE_BATCH, w.S, w.scale_block
+    split = zy.decode_split_keys(B, w.Hkv, S)
+    o = torch.empty((B, w.Hq, w.Dv), dtype=torch.bfloat16, device=qc.device)
+    ms, med = time_kernel(lambda: zy.attn_decode_fp8_paged(qc, kp, vp, qs, ksp, vsp, blk, kvl, bt, S,
+                                                            w.softmax_scale, split_keys=split, o=o),
+                          steps, warmup, stream, torch)
+    n_splits = -(-S // split)
+    kv_bytes = B * w.Hkv * S * (w.Dqk + w.Dv) + 2 * B * w.Hkv * (S // blk) * 4
+    part_bytes = 2 * n_splits * B * w.Hq * (2 * w.Dv + 4)
+    total = kv_bytes + part_bytes + B * w.Hq * (w.Dqk + 2 * w.Dv)
+    print(f"[bench] decode B={B} x {S} keys: {ms * 1e3:.1f} us ({total / ms / 1e6:.0f} GB/s)", file=sys.stderr,
+          flush=True)
+    del kp, vp, ksp, vsp
+    return {"batch": B, "kv_len": S, "heads": f"Hq={w.Hq} Hkv={w.Hkv} D={w.Dqk}", "page_size": PAGE_SIZE,
+            "split_keys": split, "n_splits": n_splits, "ms": ms, "ms_median": med,
+            "roofline": {"bound": "hbm", "achieved": total / ms / 1e6, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": total / ms / 1e6 / PEAK_HBM_GBS, "bytes_per_call": total,
+                         "kv_bytes": kv_bytes}}
+
+
 def other_workloads(names, steps, warmup, torch, zy):
     """Kernel throughput on the other benchmark shapes (4K MHA, 32K MLA, 16K activation-like
     with and without the Hadamard rotation of Q and K): FP8 exact and lean, and BF16.
@@ -399,7 +457,7 @@ def main():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-lean", action="store_true", help="skip the lean-probability FP8 mode")
     ap.add_argument("--no-others", action="store_true", help="skip the other workload shapes")
-    ap.add_argument("--no-range", action="store_true", help="skip the varlen, chunked-prefill, split-KV and paged measurements")
+    ap.add_argument("--no-range", action="store_true", help="skip the varlen, chunked-prefill, split-KV, paged and decode measurements")
     ap.add_argument("--sustain", type=float, default=4.0,
                     help="seconds of back-to-back launches per headline kernel, after 1.5 s of settling, "
                          "with clock and power telemetry (0: skip)")
@@ -587,6 +645,8 @@ def main():
                                     torch, zy)
         line["paged"] = paged_prefill(w, qc, kc, vc, qs, ks, vs, max(args.steps // 5, 5), max(args.warmup // 10, 5),
                                       stream, torch, zy)
+        line["decode"] = decode_batch(w, kc, vc, ks, vs, max(args.steps // 5, 5), max(args.warmup // 10, 5), stream,
+                                      torch, zy)
 
     if not args.no_others:
         others = [n for n in ("mha4k", "mla32k", "act16k") if n != w.name]

@@ -24,6 +24,10 @@ Functions mirror the C entry points:
   cu_seqlens, kv_lens, block_table, max_seqlen)`` / ``attn_fwd_bf16_paged``: chunks of new
   tokens (packed as in the varlen calls) against their sequences' keys in a paged cache
   [pages, Hkv, page_size, D] -> (o [Hq, T, Dv], lse or None)
+* ``attn_decode_fp8_paged(q, k_cache, v_cache, q_scale, k_cache_scale, v_cache_scale, scale_block,
+  kv_lens, block_table, max_kv_len)`` / ``attn_decode_bf16_paged``: one new token per sequence
+  (q [B, Hq, Dqk]) against its paged cache, keys split over workgroups and merged
+  -> (o [B, Hq, Dv], lse or None)
 """
 
 import math
@@ -34,7 +38,8 @@ from . import _lib
 from ._lib import ZyfaError, load
 
 __all__ = ["quantize_fp8", "attn_fwd_fp8", "attn_fwd_bf16", "attn_fwd_fp8_range", "attn_fwd_bf16_range", "attn_merge",
-           "attn_fwd_fp8_varlen", "attn_fwd_bf16_varlen", "attn_fwd_fp8_paged", "attn_fwd_bf16_paged", "ZyfaError",
+           "attn_fwd_fp8_varlen", "attn_fwd_bf16_varlen", "attn_fwd_fp8_paged", "attn_fwd_bf16_paged",
+           "attn_decode_fp8_paged", "attn_decode_bf16_paged", "decode_split_keys", "ZyfaError",
            "load", "abi_version"]
 
 
@@ -375,4 +380,96 @@ def attn_fwd_bf16_paged(q, k_cache, v_cache, cu_seqlens, kv_lens, block_table, m
     st = load().zyfa_attn_fwd_bf16_paged(pq, pk, pv, po, plse, pcu, pkl, pbt, n_seqs, int(max_seqlen), max_pages,
                                          num_pages, page_size, Hq, Hkv, T, Dqk, Dv, float(softmax_scale), _stream())
     _lib.check(st, "zyfa_attn_fwd_bf16_paged")
+    return o, lse
+
+
+def decode_split_keys(B: int, Hkv: int, max_kv_len: int, target_workgroups: int = 1024) -> int:
+    """Keys per split for the decode calls: enough splits that B * Hkv * splits reaches
+    about target_workgroups (four per compute unit of an MI355X), at least 256 keys each,
+    a multiple of 64."""
+    per = -(-max_kv_len * B * Hkv // target_workgroups)
+    return max(256, -(-per // 64) * 64)
+
+
+def _decode_common(q, k_cache, v_cache, kv_lens, block_table, max_kv_len, split_keys, o, lse, return_lse):
+    B, Hq, Dqk = q.shape
+    num_pages, Hkv, page_size, Dk = k_cache.shape
+    if Dk != Dqk or tuple(v_cache.shape[:3]) != (num_pages, Hkv, page_size):
+        raise ValueError(f"inconsistent shapes q {tuple(q.shape)} k_cache {tuple(k_cache.shape)} "
+                         f"v_cache {tuple(v_cache.shape)}")
+    pkl = _dev(kv_lens, "kv_lens", torch.int32, 1)
+    pbt = _dev(block_table, "block_table", torch.int32, 2)
+    if kv_lens.shape[0] != B or block_table.shape[0] != B:
+        raise ValueError("kv_lens and block_table need one entry / row per sequence")
+    max_pages = block_table.shape[1]
+    Dv = v_cache.shape[3]
+    if split_keys is None:
+        split_keys = decode_split_keys(B, Hkv, int(max_kv_len))
+    if o is None:
+        o = torch.empty((B, Hq, Dv), dtype=torch.bfloat16, device=q.device)
+    po = _dev(o, "o", torch.bfloat16, 3)
+    if tuple(o.shape) != (B, Hq, Dv):
+        raise ValueError("o has the wrong shape")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    plse = None
+    if lse is not None:
+        plse = _dev(lse, "lse", torch.float32, 2)
+        if tuple(lse.shape) != (B, Hq):
+            raise ValueError("lse has the wrong shape")
+    nbytes = load().zyfa_attn_decode_workspace_bytes(B, Hq, Dv, int(max_kv_len), int(split_keys))
+    ws = torch.empty(max(nbytes, 0) + 256, dtype=torch.uint8, device=q.device) if nbytes > 0 else None
+    pws = None if ws is None else (ws.data_ptr() + 255) // 256 * 256
+    return (B, Hq, Hkv, Dqk, Dv, num_pages, page_size, max_pages, int(split_keys), pkl, pbt, o, po, lse, plse, ws,
+            pws, max(nbytes, 0))
+
+
+def attn_decode_fp8_paged(q, k_cache, v_cache, q_scale, k_cache_scale, v_cache_scale, scale_block: int, kv_lens,
+                          block_table, max_kv_len: int, softmax_scale=None, split_keys=None, o=None, lse=None,
+                          return_lse: bool = False, lean: bool = False):
+    """Decode: one new token per sequence, q [B, Hq, Dqk] (e4m3 codes), at position
+    kv_lens[b] - 1 of its sequence, against the paged cache (layout as attn_fwd_fp8_paged);
+    q_scale [B, Hkv, ceil((Hq / Hkv) / scale_block)] (quantize_fp8 of q viewed as
+    [B, Hkv, Hq / Hkv, Dqk]). max_kv_len bounds kv_lens; split_keys (keys per workgroup
+    split, a multiple of 64) defaults to decode_split_keys. Returns (o bfloat16 [B, Hq, Dv],
+    lse or None)."""
+    pq = _dev(q, "q", torch.uint8, 3)
+    pk = _dev(k_cache, "k_cache", torch.uint8, 4)
+    pv = _dev(v_cache, "v_cache", torch.uint8, 4)
+    (B, Hq, Hkv, Dqk, Dv, num_pages, page_size, max_pages, split_keys, pkl, pbt, o, po, lse, plse, ws, pws,
+     nbytes) = _decode_common(q, k_cache, v_cache, kv_lens, block_table, max_kv_len, split_keys, o, lse, return_lse)
+    g = Hq // Hkv if Hkv > 0 else 0
+    nbg = (g + scale_block - 1) // scale_block if scale_block > 0 else 0
+    nbp = page_size // scale_block if scale_block > 0 else 0
+    psq = _dev(q_scale, "q_scale", torch.float32, 3)
+    psk = _dev(k_cache_scale, "k_cache_scale", torch.float32, 3)
+    psv = _dev(v_cache_scale, "v_cache_scale", torch.float32, 3)
+    if (tuple(q_scale.shape) != (B, Hkv, nbg) or tuple(k_cache_scale.shape) != (num_pages, Hkv, nbp)
+            or tuple(v_cache_scale.shape) != (num_pages, Hkv, nbp)):
+        raise ValueError("scale tensors have the wrong shape")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(Dqk)
+    st = load().zyfa_attn_decode_fp8_paged(pq, pk, pv, psq, psk, psv, scale_block, po, plse, pkl, pbt, B,
+                                           int(max_kv_len), max_pages, num_pages, page_size, Hq, Hkv, Dqk, Dv,
+                                           float(softmax_scale), split_keys, pws, nbytes, int(bool(lean)), _stream())
+    _lib.check(st, "zyfa_attn_decode_fp8_paged")
+    del ws  # (the stream orders its reuse by the caching allocator after the kernels)
+    return o, lse
+
+
+def attn_decode_bf16_paged(q, k_cache, v_cache, kv_lens, block_table, max_kv_len: int, softmax_scale=None,
+                           split_keys=None, o=None, lse=None, return_lse: bool = False):
+    """attn_decode_fp8_paged on bfloat16 tensors. Returns (o bfloat16 [B, Hq, Dv], lse or None)."""
+    pq = _dev(q, "q", torch.bfloat16, 3)
+    pk = _dev(k_cache, "k_cache", torch.bfloat16, 4)
+    pv = _dev(v_cache, "v_cache", torch.bfloat16, 4)
+    (B, Hq, Hkv, Dqk, Dv, num_pages, page_size, max_pages, split_keys, pkl, pbt, o, po, lse, plse, ws, pws,
+     nbytes) = _decode_common(q, k_cache, v_cache, kv_lens, block_table, max_kv_len, split_keys, o, lse, return_lse)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(Dqk)
+    st = load().zyfa_attn_decode_bf16_paged(pq, pk, pv, po, plse, pkl, pbt, B, int(max_kv_len), max_pages, num_pages,
+                                            page_size, Hq, Hkv, Dqk, Dv, float(softmax_scale), split_keys, pws, nbytes,
+                                            _stream())
+    _lib.check(st, "zyfa_attn_decode_bf16_paged")
+    del ws
     return o, lse

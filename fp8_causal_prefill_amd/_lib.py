@@ -32,6 +32,10 @@ _SIGNATURES = {
     "zyfa_attn_fwd_bf16_varlen": ([_vp] * 6 + [_i] * 7 + [_f, _vp], _i),
     "zyfa_attn_fwd_fp8_paged": ([_vp] * 6 + [_i] + [_vp] * 5 + [_i] * 10 + [_f, _i, _vp], _i),
     "zyfa_attn_fwd_bf16_paged": ([_vp] * 8 + [_i] * 10 + [_f, _vp], _i),
+    "zyfa_attn_decode_workspace_bytes": ([_i] * 5, ctypes.c_longlong),
+    "zyfa_attn_decode_fp8_paged": ([_vp] * 6 + [_i] + [_vp] * 4 + [_i] * 9 + [_f, _i, _vp, ctypes.c_longlong, _i, _vp],
+                                   _i),
+    "zyfa_attn_decode_bf16_paged": ([_vp] * 7 + [_i] * 9 + [_f, _i, _vp, ctypes.c_longlong, _vp], _i),
 }
 
 

@@ -75,12 +75,13 @@ constexpr int kPHeadroom = 7;
 // and subtracting that mean minimises the error of the normalised output.
 constexpr float kLeanBias = 56.0f - 0.46f;
 
-template <bool FP8, int DQK>
+template <bool FP8, int DQK, int NWAVES = 8>
 struct Cfg {
   static constexpr int DV = 128;
   // Eight waves: 256 query rows share each K/V tile copy, halving the copy traffic per
-  // FLOP against four
-  static constexpr int WAVES = 8;
+  // FLOP against four. Decode of up to 32 query heads per key/value head takes one wave:
+  // small workgroups, several per compute unit, keep more tile copies in flight.
+  static constexpr int WAVES = NWAVES;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;  // query rows per workgroup
   static constexpr int BN = 64;          // keys per tile
@@ -111,7 +112,9 @@ struct Cfg {
   static constexpr int NKS = DQK / KSTEP;
   static_assert(KSLOTS % 64 == 0 && VSLOTS % 64 == 0, "tile copies split into whole waves");
   static_assert(DQK % KSTEP == 0, "head dim must divide the MFMA depth");
-  static_assert(BM % (2 * BN) == 0, "steady iterations rely on an even number of key tiles per query tile");
+  static_assert(WAVES == 1 || BM % (2 * BN) == 0,
+                "causal prefill relies on an even number of key tiles per query tile (one-wave workgroups "
+                "serve decode only, whose rows see every key)");
 };
 
 // Key positions inside the kernel are relative to the window's first key k_begin: the
@@ -146,6 +149,12 @@ struct AttnParams {
   const int* block_table;
   const int* kv_lens;
   int max_pages, num_pages, page_shift;
+  // decode (PAGED kernels with split_keys > 0): the Sq rows of each (b, head) of Q are the
+  // query heads of one KV group, one token each at position kv_lens[b] - 1; query tile qt
+  // of the grid is the key split [qt * split_keys, (qt + 1) * split_keys), whose partial
+  // O and LSE go to rows qt * part_rows + (row of Q)
+  int split_keys;
+  size_t part_rows;
 };
 
 template <bool FP8>
@@ -156,10 +165,13 @@ using QOp = typename std::conditional<FP8, v8i, v8bf>::type;
 // 16-key run) occupy 8 consecutive rows.
 __device__ __forceinline__ int fp8_vrow(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
-template <bool FP8, int DQK, bool LEAN, bool PAGED>
-__global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(AttnParams p) {
+// (one-wave workgroups may take all 512 registers of a lane: four per compute unit, each a
+// wave of its own SIMD)
+template <bool FP8, int DQK, bool LEAN, bool PAGED, int WAVES = 8>
+__global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 2)) void attn_fwd_kernel(AttnParams p) {
   static_assert(FP8 || !LEAN, "lean probabilities are an FP8 mode");
-  using C = Cfg<FP8, DQK>;
+  static_assert(WAVES == 8 || PAGED, "one-wave workgroups serve decode only");
+  using C = Cfg<FP8, DQK, WAVES>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   char* const kring = smem;                // [2 buffers][column blocks][BN rows][64 bytes]
   char* const vring = smem + C::NBUF * C::KBUF;  // same layout for V
@@ -198,7 +210,20 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   int q_pos0 = 0;                                        // token position of query 0 (for Q scale blocks)
   size_t q_sc0 = (size_t)(b * p.Hq + hq) * p.nbq;
   size_t kv_sc0 = (size_t)(b * p.Hkv + hkv) * p.nbk;
+  size_t o_split = 0;  // decode: first row of this split's partial results in O and LSE
   if constexpr (PAGED) {
+   if (p.split_keys > 0) {
+    // decode: every row sees every key of the sequence; this workgroup takes its split of
+    // them (an empty split, or a malformed kv_lens entry, gives O = 0 and LSE = -inf,
+    // which the merge of the splits ignores)
+    const int kvl = p.kv_lens[b];
+    const int lo = qt * p.split_keys;
+    const bool ok = kvl >= 1 && kvl <= (p.max_pages << p.page_shift) && kvl <= p.n_qtiles * p.split_keys;
+    k_begin = lo;
+    Sk = ok ? max(0, min(p.split_keys, kvl - lo)) : 0;
+    dpos = kvl - 1 - lo;
+    o_split = (size_t)qt * p.part_rows;
+   } else {
     // a chunk of new tokens (rows s0 .. s1 - 1 of the packed Q) that ends sequence b's
     // kv_lens[b] cached tokens: row i sits at position kvl - L + i and sees keys up to it.
     // Malformed entries leave the chunk unwritten, as for a packed batch.
@@ -214,6 +239,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     q_pos0 = s0;
     q_sc0 = (size_t)hq * p.nbq;
     if (qt * C::BM >= Sq) return;
+   }
   } else if (p.cu_seqlens != nullptr) {
     // packed batch: sequence b is tokens s0 .. s1 - 1 of every head, causal within itself.
     // A malformed entry (a start off the key tile, decreasing, past the tensor, longer
@@ -231,7 +257,8 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     if (qt * C::BM >= Sq) return;
   }
 
-  const int q0_wg = qt * C::BM;
+  const size_t o_row0 = q_row0 + o_split;  // row of O and LSE holding query 0
+  const int q0_wg = PAGED && p.split_keys > 0 ? 0 : qt * C::BM;
   const int q0 = q0_wg + __builtin_amdgcn_readfirstlane(wave) * 32;  // (wave-uniform)
   // this lane's query row, recomputed from the lane id where needed (not kept in a register)
   auto row_of_lane = [&] { return q0 + (int)(__lane_id() & 31); };
@@ -247,12 +274,12 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   if (n == 0) {
     // no row of the workgroup sees a key of the window: O = 0, LSE = -inf
     if (my_q < Sq) {
-      uint16_t* orow = p.o + (q_row0 + my_q) * C::DV;
+      uint16_t* orow = p.o + (o_row0 + my_q) * C::DV;
 #pragma unroll
       for (int d = 0; d < 4; ++d)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) *(uint2*)(orow + 32 * d + 8 * r4 + 4 * h) = uint2{0u, 0u};
-      if (p.lse != nullptr && h == 0) p.lse[q_row0 + my_q] = -INFINITY;
+      if (p.lse != nullptr && h == 0) p.lse[o_row0 + my_q] = -INFINITY;
     }
     return;
   }
@@ -266,11 +293,11 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   // the tile's first key. Page indices are clamped to the table and the cache, so a
   // malformed table reads wrong rows, never past the tensors.
   auto page_of = [&](int t) -> int {
-    const int j = min((t * C::BN) >> p.page_shift, p.max_pages - 1);
+    const int j = min((k_begin + t * C::BN) >> p.page_shift, p.max_pages - 1);
     return min(max(p.block_table[(size_t)b * p.max_pages + j], 0), p.num_pages - 1);
   };
   auto page_row = [&](int pg, int t) -> size_t {
-    return (((size_t)pg * p.Hkv + hkv) << p.page_shift) + ((t * C::BN) & ((1 << p.page_shift) - 1));
+    return (((size_t)pg * p.Hkv + hkv) << p.page_shift) + ((k_begin + t * C::BN) & ((1 << p.page_shift) - 1));
   };
   // the pages of tiles t+1 and t+2 while iteration t runs: the page of tile t+3 is read
   // during iteration t (like the FP8 scales), so that no copy waits for the table
@@ -332,11 +359,35 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     const int r = (pos >> 2) % C::BN;
     return (pos / (4 * C::BN)) * 64 + (FP8 ? ((pos & 3) ^ (2 * ((r >> 2) & 1))) : (pos & 3)) * 16;
   };
-  uint32_t k_src[C::KCHUNKS], v_src[C::VCHUNKS];
+  // With one wave, copy i of a tile is copy 0 moved by 16 (i mod 4) rows and i / 4 column
+  // blocks (the swizzle depends on row bits 2 and 3 only): one offset register per tensor
+  // and a constant per copy, instead of a register per copy.
+  constexpr bool ONE_WAVE = C::THREADS == 64;
+  constexpr int NKSRC = ONE_WAVE ? 1 : C::KCHUNKS, NVSRC = ONE_WAVE ? 1 : C::VCHUNKS;
+  uint32_t k_src[NKSRC], v_src[NVSRC];
 #pragma unroll
-  for (int i = 0; i < C::KCHUNKS; ++i) k_src[i] = k_pos_row(i) * C::KROW + k_pos_off(i);
+  for (int i = 0; i < NKSRC; ++i) k_src[i] = k_pos_row(i) * C::KROW + k_pos_off(i);
 #pragma unroll
-  for (int i = 0; i < C::VCHUNKS; ++i) v_src[i] = v_pos_row(i) * C::VROW + v_pos_off(i);
+  for (int i = 0; i < NVSRC; ++i) v_src[i] = v_pos_row(i) * C::VROW + v_pos_off(i);
+  // (tile base, per-lane offset) of copy i
+  auto k_copy = [&](const char* tile, int i, uint32_t& off) -> const char* {
+    if constexpr (ONE_WAVE) {
+      off = k_src[0];
+      return tile + 16 * (i & 3) * C::KROW + (i >> 2) * 64;
+    } else {
+      off = k_src[i];
+      return tile;
+    }
+  };
+  auto v_copy = [&](const char* tile, int i, uint32_t& off) -> const char* {
+    if constexpr (ONE_WAVE) {
+      off = v_src[0];
+      return tile + 16 * (i & 3) * C::VROW + (i >> 2) * 64;
+    } else {
+      off = v_src[i];
+      return tile;
+    }
+  };
   const uint32_t k_lds = lds_address(kring), v_lds = lds_address(vring);
 
   // first K / V byte of key tile t (t0 = t * BN; PAGED: in cache page pg)
@@ -354,8 +405,11 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     if (t0 + C::BN <= Sk) {
       const char* tile = k_tile(t, pg);
 #pragma unroll
-      for (int i = 0; i < C::KCHUNKS; ++i)
-        if (k_live(i)) lds_copy16(tile, k_src[i], dst + i * C::THREADS * 16);
+      for (int i = 0; i < C::KCHUNKS; ++i) {
+        uint32_t off;
+        const char* base = k_copy(tile, i, off);
+        if (k_live(i)) lds_copy16(base, off, dst + i * C::THREADS * 16);
+      }
     } else {
       // rows past the window's last key repeat it (>= t0: the same tile, and page)
       const char* tile = PAGED ? k_tile(t, pg) : kbase;
@@ -373,8 +427,11 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     if (t0 + C::BN <= Sk) {
       const char* tile = v_tile(t, pg);
 #pragma unroll
-      for (int i = 0; i < C::VCHUNKS; ++i)
-        if (v_live(i)) lds_copy16(tile, v_src[i], dst + i * C::THREADS * 16);
+      for (int i = 0; i < C::VCHUNKS; ++i) {
+        uint32_t off;
+        const char* base = v_copy(tile, i, off);
+        if (v_live(i)) lds_copy16(base, off, dst + i * C::THREADS * 16);
+      }
     } else {
       const char* tile = PAGED ? v_tile(t, pg) : vbase;
       const int r0 = PAGED ? t0 : 0;
@@ -390,15 +447,21 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     const char* tile = k_tile(t, pg);
     const uint32_t dst = k_lds + buf * C::KBUF + wave_u * 64 * 16;
 #pragma unroll
-    for (int i = 0; i < C::KCHUNKS; ++i)
-      if (k_live(i)) lds_copy16(tile, k_src[i], dst + i * C::THREADS * 16);
+    for (int i = 0; i < C::KCHUNKS; ++i) {
+      uint32_t off;
+      const char* base = k_copy(tile, i, off);
+      if (k_live(i)) lds_copy16(base, off, dst + i * C::THREADS * 16);
+    }
   };
   auto fill_v_full = [&](int t, int buf, int pg) {
     const char* tile = v_tile(t, pg);
     const uint32_t dst = v_lds + buf * C::VBUF + wave_u * 64 * 16;
 #pragma unroll
-    for (int i = 0; i < C::VCHUNKS; ++i)
-      if (v_live(i)) lds_copy16(tile, v_src[i], dst + i * C::THREADS * 16);
+    for (int i = 0; i < C::VCHUNKS; ++i) {
+      uint32_t off;
+      const char* base = v_copy(tile, i, off);
+      if (v_live(i)) lds_copy16(base, off, dst + i * C::THREADS * 16);
+    }
   };
   // make this wave's copies complete before the barrier that publishes them
   auto wait_fills = [] { wait_vmem(); };
@@ -491,6 +554,22 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   wait_fills();
   __syncthreads();
 
+  // Decode: a wave whose rows all lie past the workgroup's Sq query heads has no work but
+  // its share of the tile copies; it runs only those, with the same barriers (one per
+  // iteration: copy K_{t+2}; wait for the copies and publish them; copy V_{t+1}, as every
+  // iteration of the pipelines below does, on the same buffers)
+  const bool idle = PAGED && p.split_keys > 0 && q0 >= Sq;
+  auto idle_loop = [&] {
+    for (int t = 0; t < n; ++t) {
+      const int pg3 = PAGED ? page_of(t + 3) : 0;
+      if (t + 2 < n) fill_k(t + 2, (t + 2) % C::NBUF, pg2);
+      wait_fills();
+      __syncthreads();
+      if (t + 1 < n) fill_v(t + 1, (t + 1) % C::NBUF, pg1);
+      next_pages(pg3);
+    }
+  };
+
   // key tiles that every row of the workgroup sees whole (full tiles inside the window)
   const int n_full = max(0, (min(dpos + q0_wg, Sk - 1) + 1) / C::BN);
   // iterations t < n_steady need no causal mask on tile t+1 in any wave and prefetch
@@ -519,7 +598,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
     const int my_q = row_of_lane();
     if (q0 >= Sq || my_q >= Sq) return;
     const float inv_l = l_sum > 0.0f ? 1.0f / l_sum : 0.0f;  // a row with no key: O = 0, LSE = -inf
-    uint16_t* orow = p.o + (q_row0 + my_q) * C::DV;
+    uint16_t* orow = p.o + (o_row0 + my_q) * C::DV;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -529,7 +608,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
         w.y = pack_bf16x2(oacc[d][4 * r4 + 2] * inv_l, oacc[d][4 * r4 + 3] * inv_l);
         *(uint2*)(orow + 32 * d + 8 * r4 + 4 * h) = w;
       }
-    if (p.lse != nullptr && h == 0) p.lse[q_row0 + my_q] = kLn2 * (m_ref + log2f(l_sum));
+    if (p.lse != nullptr && h == 0) p.lse[o_row0 + my_q] = kLn2 * (m_ref + log2f(l_sum));
   };
 
   if constexpr (FP8) {
@@ -833,6 +912,10 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
       next_pages(pg3);
     };
 
+    if (idle) {
+      idle_loop();
+      return;
+    }
     int t = 0;
     for (; t < n_steady; t += 2) {
       steady_step(std::false_type{}, t, sa, sb, pa, pb);
@@ -1051,6 +1134,10 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx0 = fmaxf(mx0, sc[0][r]);
     }
+    if (idle) {
+      idle_loop();
+      return;
+    }
     int t = 0;
     for (; t < n_steady_b; ++t) steady_step(std::false_type{}, t);
     for (; t + 1 < n; ++t) steady_step(std::true_type{}, t);  // the diagonal tiles
@@ -1071,9 +1158,9 @@ __global__ __launch_bounds__((Cfg<FP8, DQK>::THREADS), 2) void attn_fwd_kernel(A
   }
 }
 
-template <bool FP8, int DQK, bool LEAN = false, bool PAGED = false>
+template <bool FP8, int DQK, bool LEAN = false, bool PAGED = false, int WAVES = 8>
 static hipError_t launch(const AttnArgs& a, hipStream_t stream) {
-  using C = Cfg<FP8, DQK>;
+  using C = Cfg<FP8, DQK, WAVES>;
   AttnParams p;
   p.q = (const char*)a.q;
   p.k = (const char*)a.k;
@@ -1101,14 +1188,23 @@ static hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   p.max_pages = a.max_pages;
   p.num_pages = a.num_pages;
   p.page_shift = a.page_size == 64 ? 6 : a.page_size == 128 ? 7 : 8;
-  p.n_qtiles = ((a.cu_seqlens != nullptr ? a.max_seqlen : a.Sq) + C::BM - 1) / C::BM;
+  p.split_keys = a.split_keys;
+  p.part_rows = (size_t)a.part_rows;
+  p.n_qtiles = a.split_keys > 0 ? a.n_splits
+                                : ((a.cu_seqlens != nullptr ? a.max_seqlen : a.Sq) + C::BM - 1) / C::BM;
   p.scale_log2 = a.softmax_scale * kLog2e;
   const long long grid = (long long)p.n_qtiles * a.B * a.Hq;
-  hipLaunchKernelGGL((attn_fwd_kernel<FP8, DQK, LEAN, PAGED>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<FP8, DQK, LEAN, PAGED, WAVES>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream,
+                     p);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd_fp8(const AttnArgs& a, bool lean, hipStream_t stream) {
+  if (a.block_table != nullptr && a.split_keys > 0 && a.Sq <= 32) {  // decode, one wave per workgroup
+    if (lean)
+      return a.Dqk == 192 ? launch<true, 192, true, true, 1>(a, stream) : launch<true, 128, true, true, 1>(a, stream);
+    return a.Dqk == 192 ? launch<true, 192, false, true, 1>(a, stream) : launch<true, 128, false, true, 1>(a, stream);
+  }
   if (a.block_table != nullptr) {
     if (lean) return a.Dqk == 192 ? launch<true, 192, true, true>(a, stream) : launch<true, 128, true, true>(a, stream);
     return a.Dqk == 192 ? launch<true, 192, false, true>(a, stream) : launch<true, 128, false, true>(a, stream);
@@ -1118,6 +1214,8 @@ hipError_t launch_attn_fwd_fp8(const AttnArgs& a, bool lean, hipStream_t stream)
 }
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream) {
+  if (a.block_table != nullptr && a.split_keys > 0 && a.Sq <= 32)
+    return a.Dqk == 192 ? launch<false, 192, false, true, 1>(a, stream) : launch<false, 128, false, true, 1>(a, stream);
   if (a.block_table != nullptr)
     return a.Dqk == 192 ? launch<false, 192, false, true>(a, stream) : launch<false, 128, false, true>(a, stream);
   return a.Dqk == 192 ? launch<false, 192>(a, stream) : launch<false, 128>(a, stream);

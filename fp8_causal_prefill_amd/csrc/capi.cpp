@@ -309,6 +309,109 @@ zyfa_status zyfa_attn_fwd_bf16_paged(const uint16_t* q, const uint16_t* k_cache,
   return ok();
 }
 
+static long long decode_splits(int max_kv_len, int split_keys) { return (max_kv_len + (long long)split_keys - 1) / split_keys; }
+
+long long zyfa_attn_decode_workspace_bytes(int B, int Hq, int Dv, int max_kv_len, int split_keys) {
+  if (B <= 0 || Hq <= 0 || Dv <= 0 || max_kv_len <= 0 || split_keys <= 0) return -1;
+  const long long parts = decode_splits(max_kv_len, split_keys);
+  if (parts <= 1) return 0;
+  const long long rows = (long long)B * Hq;
+  const long long o_bytes = (parts * rows * Dv * 2 + 255) / 256 * 256;
+  return o_bytes + parts * rows * 4;
+}
+
+// Checks and launches shared by the two decode entry points: the attention kernel on
+// each key split (partial results in the workspace, or straight into o / lse when there
+// is one split), then the merge of the splits.
+static zyfa_status decode_paged(const void* q, const void* k_cache, const void* v_cache, const float* q_scale,
+                                const float* k_cache_scale, const float* v_cache_scale, int scale_block, uint16_t* o,
+                                float* lse, const int* kv_lens, const int* block_table, int B, int max_kv_len,
+                                int max_pages, int num_pages, int page_size, int Hq, int Hkv, int Dqk, int Dv,
+                                float softmax_scale, int split_keys, void* workspace, long long workspace_bytes,
+                                bool fp8, bool lean, void* stream) {
+  zyfa_status st = check_attn_common(q, k_cache, v_cache, o, lse, B, Hq, Hkv, 1, 1, 0, 0, 1, Dqk, Dv, softmax_scale);
+  if (st != ZYFA_OK) return st;
+  st = check_paged(k_cache, v_cache, kv_lens, block_table, B, max_pages, num_pages, page_size, Hkv, Dqk, Dv);
+  if (st != ZYFA_OK) return st;
+  const int g = Hq / Hkv;
+  if (g > 256) return fail(ZYFA_ERR_UNSUPPORTED, "at most 256 query heads per key/value head (got %d)", g);
+  if (max_kv_len <= 0 || (long long)max_kv_len > (long long)max_pages * page_size)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "max_kv_len (%d) must be in 1 .. max_pages * page_size", max_kv_len);
+  if (split_keys <= 0 || split_keys % zyfa::kKeyTile != 0)
+    return fail(ZYFA_ERR_INVALID_ARGUMENT, "split_keys (%d) must be a positive multiple of %d", split_keys,
+                zyfa::kKeyTile);
+  const long long parts = decode_splits(max_kv_len, split_keys);
+  if (parts * B * Hkv > 0x7FFFFFFFLL) return fail(ZYFA_ERR_UNSUPPORTED, "grid too large");
+  const long long need = zyfa_attn_decode_workspace_bytes(B, Hq, Dv, max_kv_len, split_keys);
+  if (need > 0) {
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0)
+      return fail(ZYFA_ERR_INVALID_ARGUMENT, "workspace must be non-null and 256-byte aligned");
+    if (workspace == (const void*)o || workspace == (const void*)lse || workspace == q || workspace == k_cache ||
+        workspace == v_cache)
+      return fail(ZYFA_ERR_INVALID_ARGUMENT, "workspace must not alias the inputs or outputs");
+    if (workspace_bytes < need)
+      return fail(ZYFA_ERR_INVALID_ARGUMENT, "workspace holds %lld bytes; %lld needed", workspace_bytes, need);
+  }
+  if (fp8) {
+    if (!q_scale || !k_cache_scale || !v_cache_scale)
+      return fail(ZYFA_ERR_INVALID_ARGUMENT, "scale pointers must be non-null");
+    if (!aligned16(q_scale) || !aligned16(k_cache_scale) || !aligned16(v_cache_scale))
+      return fail(ZYFA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+    if (scale_block != 64 && scale_block != 128)
+      return fail(ZYFA_ERR_INVALID_ARGUMENT, "scale_block must be 64 or 128 (got %d)", scale_block);
+    if (page_size % scale_block != 0)
+      return fail(ZYFA_ERR_INVALID_ARGUMENT, "page_size (%d) must be a multiple of scale_block (%d)", page_size,
+                  scale_block);
+  }
+  const long long rows = (long long)B * Hq;
+  uint16_t* o_parts = parts > 1 ? (uint16_t*)workspace : o;
+  float* lse_parts = parts > 1 ? (float*)((char*)workspace + (parts * rows * Dv * 2 + 255) / 256 * 256) : lse;
+  // the kernels see each KV group as one "head" whose g rows are its query heads
+  zyfa::AttnArgs a{q,        k_cache, v_cache, q_scale, k_cache_scale, v_cache_scale, o_parts, lse_parts, B, Hkv,
+                   Hkv,      g,       page_size, 0,     0,             1,             Dqk,     Dv,
+                   fp8 ? scale_block : 0, softmax_scale};
+  a.block_table = block_table;
+  a.kv_lens = kv_lens;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.page_size = page_size;
+  a.split_keys = split_keys;
+  a.n_splits = (int)parts;
+  a.part_rows = rows;
+  hipError_t e = fp8 ? zyfa::launch_attn_fwd_fp8(a, lean, (hipStream_t)stream)
+                     : zyfa::launch_attn_fwd_bf16(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ZYFA_ERR_LAUNCH, "attention launch failed: %s", hipGetErrorString(e));
+  if (parts > 1) {
+    zyfa::MergeArgs m{o_parts, lse_parts, (int)parts, o, lse, rows, Dv};
+    e = zyfa::launch_attn_merge(m, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ZYFA_ERR_LAUNCH, "merge launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+zyfa_status zyfa_attn_decode_fp8_paged(const uint8_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                       const float* q_scale, const float* k_cache_scale, const float* v_cache_scale,
+                                       int scale_block, uint16_t* o, float* lse, const int* kv_lens,
+                                       const int* block_table, int B, int max_kv_len, int max_pages, int num_pages,
+                                       int page_size, int Hq, int Hkv, int Dqk, int Dv, float softmax_scale,
+                                       int split_keys, void* workspace, long long workspace_bytes, int lean,
+                                       void* stream) {
+  if (lean != 0 && lean != 1) return fail(ZYFA_ERR_INVALID_ARGUMENT, "lean must be 0 or 1");
+  return decode_paged(q, k_cache, v_cache, q_scale, k_cache_scale, v_cache_scale, scale_block, o, lse, kv_lens,
+                      block_table, B, max_kv_len, max_pages, num_pages, page_size, Hq, Hkv, Dqk, Dv, softmax_scale,
+                      split_keys, workspace, workspace_bytes, true, lean == 1, stream);
+}
+
+zyfa_status zyfa_attn_decode_bf16_paged(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                        uint16_t* o, float* lse, const int* kv_lens, const int* block_table, int B,
+                                        int max_kv_len, int max_pages, int num_pages, int page_size, int Hq, int Hkv,
+                                        int Dqk, int Dv, float softmax_scale, int split_keys, void* workspace,
+                                        long long workspace_bytes, void* stream) {
+  return decode_paged(q, k_cache, v_cache, nullptr, nullptr, nullptr, 0, o, lse, kv_lens, block_table, B,
+                      max_kv_len, max_pages, num_pages, page_size, Hq, Hkv, Dqk, Dv, softmax_scale, split_keys,
+                      workspace, workspace_bytes, false, false, stream);
+}
+
 zyfa_status zyfa_attn_merge(const uint16_t* o_parts, const float* lse_parts, int n_parts, uint16_t* o, float* lse,
                             long long rows, int Dv, void* stream) {
   if (!o_parts || !lse_parts || !o) return fail(ZYFA_ERR_INVALID_ARGUMENT, "o_parts, lse_parts and o must be non-null");

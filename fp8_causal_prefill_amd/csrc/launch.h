@@ -32,6 +32,11 @@ struct AttnArgs {
   const int* block_table = nullptr;
   const int* kv_lens = nullptr;
   int max_pages = 0, num_pages = 0, page_size = 0;
+  // decode over a paged cache (split_keys > 0, with block_table): Sq query heads per KV
+  // head in each row group of Q; n_splits key splits of split_keys keys, partial results in
+  // o / lse at rows split * part_rows + row
+  int split_keys = 0, n_splits = 0;
+  long long part_rows = 0;
 };
 
 // keys per tile of the attention kernels: a key window must start on a tile boundary

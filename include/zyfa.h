@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define ZYFA_ABI_VERSION 4
+#define ZYFA_ABI_VERSION 5
 
 typedef enum zyfa_status {
   ZYFA_OK = 0,
@@ -299,6 +299,55 @@ zyfa_status zyfa_attn_fwd_bf16_paged(const uint16_t* q, const uint16_t* k_cache,
                                      const int* block_table, int n_seqs, int max_seqlen, int max_pages,
                                      int num_pages, int page_size, int Hq, int Hkv, int T, int Dqk, int Dv,
                                      float softmax_scale, void* stream);
+
+/*
+ * zyfa_attn_decode_fp8_paged / zyfa_attn_decode_bf16_paged -- one new token per sequence
+ * against its paged key/value cache (decode).
+ *
+ * Source: ZYFA page, "Future Work" (decode support, paged KV caches); the split of the
+ * keys and the log-sum-exp merge follow Zyphra "Inference Wave 2", section on CSA
+ * dual-scope decode. Sequence b's new token is its last, at position kv_lens[b] - 1, and
+ * sees all kv_lens[b] keys (its own key and value already in the cache). The keys are
+ * cut into splits of split_keys keys; the attention kernel runs once per (sequence, KV
+ * head, split) with the KV group's Hq / Hkv query heads as its rows, writes each split's
+ * partial result to the workspace, and zyfa_attn_merge's kernel combines the splits.
+ *
+ *   q            [B, Hq, Dqk]: the new tokens' queries (FP8: e4m3 codes).
+ *   q_scale      FP8: [B, Hkv, ceil((Hq / Hkv) / scale_block)]: one scale per block of
+ *                the query heads of a KV group, the layout zyfa_quantize_fp8 writes for q
+ *                viewed as [B, Hkv, Hq / Hkv, Dqk].
+ *   k_cache, v_cache, k_cache_scale, v_cache_scale, block_table, page_size, num_pages,
+ *                max_pages  as in zyfa_attn_fwd_fp8_paged (block_table [B, max_pages]).
+ *   kv_lens      device int32 [B]: 1 <= kv_lens[b] <= max_kv_len.
+ *   max_kv_len   host bound on kv_lens, 1 .. max_pages * page_size; sizes the grid.
+ *   split_keys   keys per split: a positive multiple of 64. There are
+ *                ceil(max_kv_len / split_keys) splits.
+ *   workspace    device memory of zyfa_attn_decode_workspace_bytes(B, Hq, Dv, max_kv_len,
+ *                split_keys) bytes, 256-byte aligned (none is needed, and NULL is
+ *                accepted, with one split); its contents on entry do not matter.
+ *   o, lse       out: [B, Hq, Dv] bfloat16 and (may be NULL) [B, Hq] float32.
+ *   Hq / Hkv     at most 256.
+ *
+ * The splits' partial outputs are rounded to bfloat16 before the merge. A sequence whose
+ * kv_lens entry breaks the rules gets O = 0 and LSE = -inf (no error is reported).
+ * Other rules (pointers, alignment, streams, errors, head shapes, lean, block_table
+ * clamping) as zyfa_attn_fwd_fp8_paged. Two kernels are enqueued on the stream.
+ */
+long long zyfa_attn_decode_workspace_bytes(int B, int Hq, int Dv, int max_kv_len, int split_keys);
+
+zyfa_status zyfa_attn_decode_fp8_paged(const uint8_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                       const float* q_scale, const float* k_cache_scale, const float* v_cache_scale,
+                                       int scale_block, uint16_t* o, float* lse, const int* kv_lens,
+                                       const int* block_table, int B, int max_kv_len, int max_pages, int num_pages,
+                                       int page_size, int Hq, int Hkv, int Dqk, int Dv, float softmax_scale,
+                                       int split_keys, void* workspace, long long workspace_bytes, int lean,
+                                       void* stream);
+
+zyfa_status zyfa_attn_decode_bf16_paged(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                        uint16_t* o, float* lse, const int* kv_lens, const int* block_table, int B,
+                                        int max_kv_len, int max_pages, int num_pages, int page_size, int Hq, int Hkv,
+                                        int Dqk, int Dv, float softmax_scale, int split_keys, void* workspace,
+                                        long long workspace_bytes, void* stream);
 
 /*
  * zyfa_attn_merge -- combine partial attention results over disjoint key sets.

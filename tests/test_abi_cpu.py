@@ -39,14 +39,15 @@ def test_exports_every_declared_symbol(lib):
                           "zyfa_attn_fwd_fp8", "zyfa_attn_fwd_fp8_lean", "zyfa_attn_fwd_bf16",
                           "zyfa_attn_fwd_fp8_range", "zyfa_attn_fwd_bf16_range", "zyfa_attn_merge",
                           "zyfa_attn_fwd_fp8_varlen", "zyfa_attn_fwd_bf16_varlen", "zyfa_attn_fwd_fp8_paged",
-                          "zyfa_attn_fwd_bf16_paged"}
+                          "zyfa_attn_fwd_bf16_paged", "zyfa_attn_decode_workspace_bytes", "zyfa_attn_decode_fp8_paged",
+                          "zyfa_attn_decode_bf16_paged"}
     raw = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.zyfa_abi_version() == 4
+    assert lib.zyfa_abi_version() == 5
     assert lib.zyfa_status_string(0) == b"ZYFA_OK"
     assert lib.zyfa_status_string(1) == b"ZYFA_ERR_INVALID_ARGUMENT"
     assert lib.zyfa_status_string(2) == b"ZYFA_ERR_UNSUPPORTED"
@@ -183,6 +184,48 @@ def test_paged_argument_checks(lib, kw, expect):
 @pytest.mark.parametrize("kw", [dict(qs=None), dict(ks=MIS), dict(blk=32), dict(lean=2), dict(page=64, blk=128)])
 def test_fp8_paged_scale_and_mode_checks(lib, kw):
     assert fp8_paged(lib, **kw) == INVALID
+
+
+WS = 0x1000000  # a 256-byte-aligned fake workspace
+
+
+def fp8_decode(lib, q=P, k=P2, v=P3, qs=P4, ks=P5, vs=P6, blk=128, o=P7, lse=None, kvl=0x90000, bt=0xA0000, B=4,
+               maxkv=1000, maxp=8, nump=30, page=128, Hq=8, Hkv=2, Dqk=128, Dv=128, scale=0.088, split=256, ws=WS,
+               wsb=1 << 30, lean=0):
+    return lib.zyfa_attn_decode_fp8_paged(q, k, v, qs, ks, vs, blk, o, lse, kvl, bt, B, maxkv, maxp, nump, page, Hq,
+                                          Hkv, Dqk, Dv, scale, split, ws, wsb, lean, None)
+
+
+def bf16_decode(lib, q=P, k=P2, v=P3, o=P7, lse=None, kvl=0x90000, bt=0xA0000, B=4, maxkv=1000, maxp=8, nump=30,
+                page=128, Hq=8, Hkv=2, Dqk=128, Dv=128, scale=0.088, split=256, ws=WS, wsb=1 << 30):
+    return lib.zyfa_attn_decode_bf16_paged(q, k, v, o, lse, kvl, bt, B, maxkv, maxp, nump, page, Hq, Hkv, Dqk, Dv,
+                                           scale, split, ws, wsb, None)
+
+
+def test_decode_workspace_bytes(lib):
+    f = lib.zyfa_attn_decode_workspace_bytes
+    assert f(4, 8, 128, 1000, 256) == (4 * 4 * 8 * 128 * 2 + 255) // 256 * 256 + 4 * 4 * 8 * 4
+    assert f(4, 8, 128, 256, 256) == 0        # one split: results go straight to o / lse
+    assert f(0, 8, 128, 1000, 256) == -1 and f(4, 8, 128, 1000, 0) == -1
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID), (dict(o=MIS), INVALID), (dict(kvl=None), INVALID), (dict(bt=0xA0002), INVALID),
+    (dict(B=0), INVALID), (dict(maxkv=0), INVALID), (dict(maxkv=1025), INVALID), (dict(page=96), INVALID),
+    (dict(split=0), INVALID), (dict(split=100), INVALID), (dict(ws=None), INVALID), (dict(ws=WS + 16), INVALID),
+    (dict(wsb=1000), INVALID), (dict(ws=P7), INVALID), (dict(Hq=6, Hkv=4), INVALID),
+    (dict(Hq=512, Hkv=1), UNSUPPORTED), (dict(scale=-1.0), INVALID), (dict(Dqk=64, Dv=64), UNSUPPORTED),
+    (dict(o=P), INVALID),
+])
+def test_decode_argument_checks(lib, kw, expect):
+    assert bf16_decode(lib, **kw) == expect
+    assert lib.zyfa_last_error() != b""
+    assert fp8_decode(lib, **kw) == expect
+
+
+@pytest.mark.parametrize("kw", [dict(qs=None), dict(vs=MIS), dict(blk=32), dict(lean=2), dict(page=64, blk=128)])
+def test_fp8_decode_scale_and_mode_checks(lib, kw):
+    assert fp8_decode(lib, **kw) == INVALID
 
 
 def merge(lib, op=P, lp=P2, n=2, o=P3, lse=None, rows=1000, Dv=128):

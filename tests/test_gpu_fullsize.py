@@ -242,3 +242,47 @@ def test_full_size_paged_prefill():
         ref_heads.append(ro[0, 0])
         got_heads.append(bf16_from_f64(o_c[hq, torch.from_numpy(rows).to(dev)]))
     _check("gqa32k paged chunk", got_heads, ref_heads, rows_e, rows_l, BARS["fp8"])
+
+
+def test_full_size_decode_batch():
+    """The decode measurement of the benchmark: 8 sequences of 32K keys in a shuffled page
+    cache at the headline heads (FP8 exact, the split and merge the benchmark times). Every
+    output against the oracle on the pages it gathers (one-token chunks at position
+    32767)."""
+    from oracle import gather_pages, window_attention
+    import bench
+    w = WORKLOADS["gqa32k"]
+    print("case: gqa32k decode batch", flush=True)
+    _, k, v = generate(w, seed=0)
+    dev = "cuda"
+    kd, vd = (torch.from_numpy(x).to(dev) for x in (k, v))
+    del k, v
+    blk, S = w.scale_block, w.S
+    kc, ks = zy.quantize_fp8(kd, blk)
+    vc, vs = zy.quantize_fp8(vd, blk)
+    del kd, vd
+    qc, qs, kp, vp, ksp, vsp, kvl, bt = bench.decode_setup(w, kc, vc, ks, vs, torch, zy)
+    B = qc.shape[0]
+    split = zy.decode_split_keys(B, w.Hkv, S)
+    o, lse = zy.attn_decode_fp8_paged(qc, kp, vp, qs, ksp, vsp, blk, kvl, bt, S, w.softmax_scale, split_keys=split,
+                                      return_lse=True)
+    torch.cuda.synchronize()
+    g = w.Hq // w.Hkv
+    qq = dequantize_blocks(qc.reshape(B, w.Hkv, g, w.Dqk).cpu().numpy(), qs.cpu().numpy(), blk)  # [B, Hkv, g, D]
+    table = bt.cpu().numpy()
+    got, ref = [], []
+    for b in (0, B - 1):
+        # the sequence's pages, in table order, dequantized; then laid end to end
+        pages = torch.from_numpy(table[b].astype(np.int64)).to(dev)
+        for hk in range(w.Hkv):
+            kk, vv = (dequantize_blocks(c[pages, hk:hk + 1].cpu().numpy(), s_[pages, hk:hk + 1].cpu().numpy(), blk)
+                      for c, s_ in ((kp, ksp), (vp, vsp)))
+            ident = np.arange(len(table[b]))
+            kg, vg = gather_pages(kk, ident, S), gather_pages(vv, ident, S)  # [1, S, D]
+            ro, _ = window_attention(qq[b, hk][None, :, None], kg[None], vg[None], w.softmax_scale, q_offset=S - 1)
+            ref.append(ro[0, :, 0])
+            got.append(bf16_from_f64(o[b, hk * g:(hk + 1) * g]))
+    got, ref = np.stack(got), np.stack(ref)
+    err = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    print(f"gqa32k decode rel-L2 {err:.3e}")
+    assert err <= BARS["fp8"]
