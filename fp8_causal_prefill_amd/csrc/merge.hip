@@ -33,11 +33,15 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const uint16_
   const int sub = threadIdx.x % LANES;
   const long long stride = (long long)gridDim.x * ROWS_PER_BLOCK;
   for (long long r = (long long)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / LANES; r < rows; r += stride) {
+    // (the part loops are unrolled so that several parts' loads are in flight at once: a
+    // decode merge has few rows and many parts; the sums keep their order)
     float m = -INFINITY;
+#pragma unroll 8
     for (int p = 0; p < n_parts; ++p) m = fmaxf(m, lse_parts[(long long)p * rows + r]);
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     float wsum = 0.0f;
     if (m > -INFINITY) {
+#pragma unroll 8
       for (int p = 0; p < n_parts; ++p) {
         const float w = expf(lse_parts[(long long)p * rows + r] - m);  // exp(-inf) = 0
         wsum += w;
