@@ -133,3 +133,19 @@ def test_decode_split_invariance_and_malformed(mode):
     assert np.all(o3[[2, 4]] == 0.0) and np.all(l3[[2, 4]] == -np.inf)
     keep = [i for i in range(d.B) if i not in (2, 4)]
     assert rel_l2(o3[keep], o1[keep]) < 4e-3
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp8"])
+def test_decode_large_group_on_the_eight_wave_workgroup(mode):
+    # 64 query heads per KV head: more rows than one wave holds, so the eight-wave
+    # workgroup runs, with six waves past the rows taking only their share of the copies
+    Hq, Hkv, D, P = 64, 1, 128, 128
+    _case(mode, "64 heads per KV head")
+    d = Decode([1, 65, 700, 2048], P, Hq, Hkv, D, D, seed=4)
+    for sk in (128, 4096):
+        og, lg, deq = d.run(mode, block=64, split_keys=sk)
+        ro, rl = d.oracle(deq, 1 / math.sqrt(D))
+        err = rel_l2(og, ro)
+        print(f"{mode} split {sk} rel-L2 {err:.3e}")
+        assert err <= BARS[mode]
+        assert np.abs(lg - rl).max() < (1e-3 if mode == "bf16" else math.log(1 + 2 ** -4))
