@@ -5,7 +5,10 @@
  *
  *     O = softmax(Q K^T * softmax_scale + causal mask) V
  *
- * for equal query and key lengths, in two precisions:
+ * for equal query and key lengths (and, through the entry points further down, for a
+ * chunk of query rows against a key window, packed batches of sequences, chunks and
+ * single decode tokens against a paged key/value cache, and the merge of partial
+ * results), in two precisions:
  *
  *   - FP8: Q, K, V as OCP e4m3 (E4M3FN) codes with one float32 scale per
  *     (batch, head, block of scale_block tokens);
@@ -25,12 +28,14 @@
  * Conventions shared by every entry point:
  *
  *   Layout     Every tensor is dense row-major [B, H, S, D] (D fastest), the
- *              order of PyTorch's scaled_dot_product_attention. Scales are dense
- *              [B, H, nb] with nb = ceil(S / scale_block). Query head h reads
- *              key/value head h / (Hq / Hkv).
+ *              order of PyTorch's scaled_dot_product_attention, unless an entry
+ *              point states otherwise (packed batches, paged caches, decode).
+ *              Scales are dense [B, H, nb] with nb = ceil(S / scale_block). Query
+ *              head h reads key/value head h / (Hq / Hkv).
  *   Memory     All pointers are device pointers owned by the caller and must be
  *              16-byte aligned. Outputs must not alias inputs. The library never
- *              allocates, frees or synchronises.
+ *              allocates, frees or synchronises (decode takes its scratch space
+ *              from a caller's workspace).
  *   Streams    `stream` is a hipStream_t passed as void* (NULL = the null stream);
  *              all work is enqueued on it and the call returns without waiting.
  *   Errors     Argument checks happen on the host before any device work; a
