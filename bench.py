@@ -347,10 +347,12 @@ DECODE_BATCH = 8
 
 def decode_setup(w, kc, vc, ks, vs, torch, zy, seed=1):
     """Decode inputs at the benchmark's heads: DECODE_BATCH sequences of S tokens each, every
-    one holding the benchmark's FP8 keys and values in its own PAGE_SIZE-token pages of one
+    one holding the benchmark's keys and values in its own PAGE_SIZE-token pages of one
     shared cache (seeded random page order), and one new query per sequence and head
-    (seeded Gaussian, quantized with one scale per KV group). Returns (q codes [B, Hq, D],
-    q scales, k cache, v cache, k scales, v scales, kv_lens, block table)."""
+    (seeded Gaussian). FP8 (ks, vs given): kc, vc are codes, the query is quantized with
+    one scale per KV group; BF16 (ks = vs = None): kc, vc are bfloat16. Returns (q [B, Hq,
+    D], q scales or None, k cache, v cache, k scales or None, v scales or None, kv_lens,
+    block table)."""
     from workloads import custom, generate, page_table
     B, S, P, blk, dev = DECODE_BATCH, w.S, PAGE_SIZE, w.scale_block, kc.device
     table, num_pages = page_table([S] * B, P, seed=seed)
@@ -366,17 +368,21 @@ def decode_setup(w, kc, vc, ks, vs, torch, zy, seed=1):
     g = w.Hq // w.Hkv
     q, _, _ = generate(custom(1, B, B, w.Hq, w.Dqk, w.Dv, wid=950), seed=seed)
     qd = torch.from_numpy(q[0]).to(dev).reshape(B, w.Hkv, g, w.Dqk)
-    qc, qs = zy.quantize_fp8(qd, blk)
     kvl = torch.full((B,), S, dtype=torch.int32, device=dev)
+    if ks is None:
+        return (qd.reshape(B, w.Hq, w.Dqk).to(torch.bfloat16), None, to_pages(kc, P), to_pages(vc, P), None, None,
+                kvl, bt)
+    qc, qs = zy.quantize_fp8(qd, blk)
     return (qc.reshape(B, w.Hq, w.Dqk), qs, to_pages(kc, P), to_pages(vc, P), to_pages(ks, P // blk),
             to_pages(vs, P // blk), kvl, bt)
 
 
-def decode_batch(w, kc, vc, ks, vs, steps, warmup, stream, torch, zy):
-    """The decode entry point (FP8 exact) on decode_setup's batch: one call is the split
-    attention kernel plus the merge. HBM-bound: algorithmic bytes per call are the cached
-    keys and values (codes and scales) of every sequence, the queries, the partial results
-    (written and read once) and the output."""
+def decode_batch(w, kc, vc, ks, vs, kd, vd, steps, warmup, stream, torch, zy):
+    """The decode entry points on decode_setup's batch, FP8 exact (kc, vc, ks, vs) and BF16
+    (kd, vd as bfloat16): one call is the split attention kernel plus the merge.
+    HBM-bound: algorithmic bytes per call are the cached keys and values (codes and
+    scales) of every sequence, the queries, the partial results (written and read once)
+    and the output."""
     if w.B != 1 or w.S % PAGE_SIZE != 0:
         return None
     qc, qs, kp, vp, ksp, vsp, kvl, bt = decode_setup(w, kc, vc, ks, vs, torch, zy)
@@ -392,12 +398,23 @@ def decode_batch(w, kc, vc, ks, vs, steps, warmup, stream, torch, zy):
     total = kv_bytes + part_bytes + B * w.Hq * (w.Dqk + 2 * w.Dv)
     print(f"[bench] decode B={B} x {S} keys: {ms * 1e3:.1f} us ({total / ms / 1e6:.0f} GB/s)", file=sys.stderr,
           flush=True)
-    del kp, vp, ksp, vsp
-    return {"batch": B, "kv_len": S, "heads": f"Hq={w.Hq} Hkv={w.Hkv} D={w.Dqk}", "page_size": PAGE_SIZE,
-            "split_keys": split, "n_splits": n_splits, "ms": ms, "ms_median": med,
-            "roofline": {"bound": "hbm", "achieved": total / ms / 1e6, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": total / ms / 1e6 / PEAK_HBM_GBS, "bytes_per_call": total,
-                         "kv_bytes": kv_bytes}}
+    del kp, vp, ksp, vsp, qc
+    rec = {"batch": B, "kv_len": S, "heads": f"Hq={w.Hq} Hkv={w.Hkv} D={w.Dqk}", "page_size": PAGE_SIZE,
+           "split_keys": split, "n_splits": n_splits, "ms": ms, "ms_median": med,
+           "roofline": {"bound": "hbm", "achieved": total / ms / 1e6, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": total / ms / 1e6 / PEAK_HBM_GBS, "bytes_per_call": total,
+                        "kv_bytes": kv_bytes}}
+    # BF16: the same batch in bfloat16 (twice the cache bytes, no scales)
+    qb, _, kpb, vpb, _, _, kvl, bt = decode_setup(w, kd.to(torch.bfloat16), vd.to(torch.bfloat16), None, None,
+                                                   torch, zy)
+    ms_b, med_b = time_kernel(lambda: zy.attn_decode_bf16_paged(qb, kpb, vpb, kvl, bt, S, w.softmax_scale,
+                                                                 split_keys=split, o=o), steps, warmup, stream, torch)
+    total_b = 2 * B * w.Hkv * S * (w.Dqk + w.Dv) + part_bytes + B * w.Hq * (2 * w.Dqk + 2 * w.Dv)
+    print(f"[bench] decode bf16: {ms_b * 1e3:.1f} us ({total_b / ms_b / 1e6:.0f} GB/s)", file=sys.stderr, flush=True)
+    rec["bf16"] = {"ms": ms_b, "ms_median": med_b, "achieved_gbs": total_b / ms_b / 1e6,
+                   "frac_of_hbm": total_b / ms_b / 1e6 / PEAK_HBM_GBS, "bytes_per_call": total_b}
+    del kpb, vpb
+    return rec
 
 
 def other_workloads(names, steps, warmup, torch, zy):
@@ -645,8 +662,8 @@ def main():
                                     torch, zy)
         line["paged"] = paged_prefill(w, qc, kc, vc, qs, ks, vs, max(args.steps // 5, 5), max(args.warmup // 10, 5),
                                       stream, torch, zy)
-        line["decode"] = decode_batch(w, kc, vc, ks, vs, max(args.steps // 5, 5), max(args.warmup // 10, 5), stream,
-                                      torch, zy)
+        line["decode"] = decode_batch(w, kc, vc, ks, vs, kd, vd, max(args.steps // 5, 5), max(args.warmup // 10, 5),
+                                      stream, torch, zy)
 
     if not args.no_others:
         others = [n for n in ("mha4k", "mla32k", "act16k") if n != w.name]

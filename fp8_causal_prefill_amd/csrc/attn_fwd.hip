@@ -79,8 +79,8 @@ template <bool FP8, int DQK, int NWAVES = 8>
 struct Cfg {
   static constexpr int DV = 128;
   // Eight waves: 256 query rows share each K/V tile copy, halving the copy traffic per
-  // FLOP against four. Decode of up to 32 query heads per key/value head takes one wave:
-  // small workgroups, several per compute unit, keep more tile copies in flight.
+  // FLOP against four. FP8 decode of up to 32 query heads per key/value head takes one
+  // wave: small workgroups, several per compute unit, keep more tile copies in flight.
   static constexpr int WAVES = NWAVES;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;  // query rows per workgroup
@@ -170,7 +170,7 @@ __device__ __forceinline__ int fp8_vrow(int k) { return (k & ~12) | ((k & 4) << 
 template <bool FP8, int DQK, bool LEAN, bool PAGED, int WAVES = 8>
 __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 2)) void attn_fwd_kernel(AttnParams p) {
   static_assert(FP8 || !LEAN, "lean probabilities are an FP8 mode");
-  static_assert(WAVES == 8 || PAGED, "one-wave workgroups serve decode only");
+  static_assert(WAVES == 8 || (PAGED && FP8), "one-wave workgroups serve FP8 decode only");
   using C = Cfg<FP8, DQK, WAVES>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   char* const kring = smem;                // [2 buffers][column blocks][BN rows][64 bytes]
@@ -1214,8 +1214,8 @@ hipError_t launch_attn_fwd_fp8(const AttnArgs& a, bool lean, hipStream_t stream)
 }
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream) {
-  if (a.block_table != nullptr && a.split_keys > 0 && a.Sq <= 32)
-    return a.Dqk == 192 ? launch<false, 192, false, true, 1>(a, stream) : launch<false, 128, false, true, 1>(a, stream);
+  // (BF16 decode stays on the eight-wave workgroup: a one-wave BF16 workgroup measured
+  // four times slower)
   if (a.block_table != nullptr)
     return a.Dqk == 192 ? launch<false, 192, false, true>(a, stream) : launch<false, 128, false, true>(a, stream);
   return a.Dqk == 192 ? launch<false, 192>(a, stream) : launch<false, 128>(a, stream);
