@@ -558,7 +558,10 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
   // its share of the tile copies; it runs only those, with the same barriers (one per
   // iteration: copy K_{t+2}; wait for the copies and publish them; copy V_{t+1}, as every
   // iteration of the pipelines below does, on the same buffers)
-  const bool idle = PAGED && p.split_keys > 0 && q0 >= Sq;
+  // (BF16 only: in the FP8 instantiations the extra path cost the paged kernels at the MLA
+  // shape five more spilled registers, and an FP8 group of more than 32 query heads, the
+  // only FP8 decode on eight waves, is rare; its surplus waves compute clamped rows)
+  const bool idle = PAGED && !FP8 && p.split_keys > 0 && q0 >= Sq;
   auto idle_loop = [&] {
     for (int t = 0; t < n; ++t) {
       const int pg3 = PAGED ? page_of(t + 3) : 0;
@@ -912,10 +915,6 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
       next_pages(pg3);
     };
 
-    if (idle) {
-      idle_loop();
-      return;
-    }
     int t = 0;
     for (; t < n_steady; t += 2) {
       steady_step(std::false_type{}, t, sa, sb, pa, pb);

@@ -138,7 +138,8 @@ def test_decode_split_invariance_and_malformed(mode):
 @pytest.mark.parametrize("mode", ["bf16", "fp8"])
 def test_decode_large_group_on_the_eight_wave_workgroup(mode):
     # 64 query heads per KV head: more rows than one wave holds, so the eight-wave
-    # workgroup runs, with six waves past the rows taking only their share of the copies
+    # workgroup runs; six of its waves lie past the rows (BF16: they take only their share
+    # of the copies; FP8: they compute clamped rows that are not stored)
     Hq, Hkv, D, P = 64, 1, 128, 128
     _case(mode, "64 heads per KV head")
     d = Decode([1, 65, 700, 2048], P, Hq, Hkv, D, D, seed=4)
