@@ -316,6 +316,7 @@ long long zyfa_attn_decode_workspace_bytes(int B, int Hq, int Dv, int max_kv_len
   const long long parts = decode_splits(max_kv_len, split_keys);
   if (parts <= 1) return 0;
   const long long rows = (long long)B * Hq;
+  if (rows * (2LL * Dv + 4) > (1LL << 60) / parts) return -1;  // (no overflow below)
   const long long o_bytes = (parts * rows * Dv * 2 + 255) / 256 * 256;
   return o_bytes + parts * rows * 4;
 }

@@ -338,6 +338,8 @@ zyfa_status zyfa_attn_fwd_bf16_paged(const uint16_t* q, const uint16_t* k_cache,
  * Other rules (pointers, alignment, streams, errors, head shapes, lean, block_table
  * clamping) as zyfa_attn_fwd_fp8_paged. Two kernels are enqueued on the stream.
  */
+/* Workspace bytes a decode call with these sizes needs (0 with one split), or -1 for
+ * non-positive sizes or a workspace beyond 2^60 bytes. */
 long long zyfa_attn_decode_workspace_bytes(int B, int Hq, int Dv, int max_kv_len, int split_keys);
 
 zyfa_status zyfa_attn_decode_fp8_paged(const uint8_t* q, const uint8_t* k_cache, const uint8_t* v_cache,

@@ -207,6 +207,7 @@ def test_decode_workspace_bytes(lib):
     assert f(4, 8, 128, 1000, 256) == (4 * 4 * 8 * 128 * 2 + 255) // 256 * 256 + 4 * 4 * 8 * 4
     assert f(4, 8, 128, 256, 256) == 0        # one split: results go straight to o / lse
     assert f(0, 8, 128, 1000, 256) == -1 and f(4, 8, 128, 1000, 0) == -1
+    assert f(1 << 30, 1 << 30, 512, 1 << 30, 64) == -1  # would overflow
 
 
 @pytest.mark.parametrize("kw,expect", [
