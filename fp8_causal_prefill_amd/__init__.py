@@ -385,13 +385,16 @@ def attn_fwd_bf16_paged(q, k_cache, v_cache, cu_seqlens, kv_lens, block_table, m
 
 def decode_split_keys(B: int, Hkv: int, max_kv_len: int, target_workgroups: int = 1024) -> int:
     """Keys per split for the decode calls: enough splits that B * Hkv * splits reaches
-    about target_workgroups (four per compute unit of an MI355X), at least 256 keys each,
-    a multiple of 64."""
+    about target_workgroups, at least 256 keys each, a multiple of 64. The default, 1024,
+    is four workgroups per compute unit of an MI355X, what the one-wave FP8 decode
+    workgroup (up to 32 query heads per KV head) fits; the eight-wave workgroup (BF16, or
+    larger groups) fits one, and its calls default to 256."""
     per = -(-max_kv_len * B * Hkv // target_workgroups)
     return max(256, -(-per // 64) * 64)
 
 
-def _decode_common(q, k_cache, v_cache, kv_lens, block_table, max_kv_len, split_keys, o, lse, return_lse):
+def _decode_common(q, k_cache, v_cache, kv_lens, block_table, max_kv_len, split_keys, o, lse, return_lse,
+                   one_wave):
     B, Hq, Dqk = q.shape
     num_pages, Hkv, page_size, Dk = k_cache.shape
     if Dk != Dqk or tuple(v_cache.shape[:3]) != (num_pages, Hkv, page_size):
@@ -404,7 +407,7 @@ def _decode_common(q, k_cache, v_cache, kv_lens, block_table, max_kv_len, split_
     max_pages = block_table.shape[1]
     Dv = v_cache.shape[3]
     if split_keys is None:
-        split_keys = decode_split_keys(B, Hkv, int(max_kv_len))
+        split_keys = decode_split_keys(B, Hkv, int(max_kv_len), 1024 if one_wave else 256)
     if o is None:
         o = torch.empty((B, Hq, Dv), dtype=torch.bfloat16, device=q.device)
     po = _dev(o, "o", torch.bfloat16, 3)
@@ -437,7 +440,8 @@ def attn_decode_fp8_paged(q, k_cache, v_cache, q_scale, k_cache_scale, v_cache_s
     pk = _dev(k_cache, "k_cache", torch.uint8, 4)
     pv = _dev(v_cache, "v_cache", torch.uint8, 4)
     (B, Hq, Hkv, Dqk, Dv, num_pages, page_size, max_pages, split_keys, pkl, pbt, o, po, lse, plse, ws, pws,
-     nbytes) = _decode_common(q, k_cache, v_cache, kv_lens, block_table, max_kv_len, split_keys, o, lse, return_lse)
+     nbytes) = _decode_common(q, k_cache, v_cache, kv_lens, block_table, max_kv_len, split_keys, o, lse, return_lse,
+                              q.shape[1] <= 32 * k_cache.shape[1])
     g = Hq // Hkv if Hkv > 0 else 0
     nbg = (g + scale_block - 1) // scale_block if scale_block > 0 else 0
     nbp = page_size // scale_block if scale_block > 0 else 0
@@ -464,7 +468,8 @@ def attn_decode_bf16_paged(q, k_cache, v_cache, kv_lens, block_table, max_kv_len
     pk = _dev(k_cache, "k_cache", torch.bfloat16, 4)
     pv = _dev(v_cache, "v_cache", torch.bfloat16, 4)
     (B, Hq, Hkv, Dqk, Dv, num_pages, page_size, max_pages, split_keys, pkl, pbt, o, po, lse, plse, ws, pws,
-     nbytes) = _decode_common(q, k_cache, v_cache, kv_lens, block_table, max_kv_len, split_keys, o, lse, return_lse)
+     nbytes) = _decode_common(q, k_cache, v_cache, kv_lens, block_table, max_kv_len, split_keys, o, lse, return_lse,
+                              False)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(Dqk)
     st = load().zyfa_attn_decode_bf16_paged(pq, pk, pv, po, plse, pkl, pbt, B, int(max_kv_len), max_pages, num_pages,
