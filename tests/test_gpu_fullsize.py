@@ -286,3 +286,41 @@ def test_full_size_decode_batch():
     err = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
     print(f"gqa32k decode rel-L2 {err:.3e}")
     assert err <= BARS["fp8"]
+
+
+def test_full_size_decode_batch_bf16():
+    """The BF16 decode measurement of the benchmark: the same batch as the FP8 one in
+    bfloat16, with the split size the benchmark uses for it; the outputs of two sequences
+    against the oracle on the pages it gathers."""
+    from oracle import gather_pages, window_attention
+    import bench
+    w = WORKLOADS["gqa32k"]
+    print("case: gqa32k decode batch bf16", flush=True)
+    _, k, v = generate(w, seed=0)
+    dev = "cuda"
+    kd, vd = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (k, v))
+    del k, v
+    S = w.S
+    qb, _, kp, vp, _, _, kvl, bt = bench.decode_setup(w, kd, vd, None, None, torch, zy)
+    del kd, vd
+    B = qb.shape[0]
+    split = zy.decode_split_keys(B, w.Hkv, S, 256)
+    o, _ = zy.attn_decode_bf16_paged(qb, kp, vp, kvl, bt, S, w.softmax_scale, split_keys=split)
+    torch.cuda.synchronize()
+    g = w.Hq // w.Hkv
+    qq = qb.float().cpu().numpy().astype(np.float64).reshape(B, w.Hkv, g, w.Dqk)
+    table = bt.cpu().numpy()
+    got, ref = [], []
+    for b in (0, B - 1):
+        pages = torch.from_numpy(table[b].astype(np.int64)).to(dev)
+        ident = np.arange(len(table[b]))
+        for hk in range(w.Hkv):
+            kk, vv = (c[pages, hk:hk + 1].float().cpu().numpy().astype(np.float64) for c in (kp, vp))
+            kg, vg = gather_pages(kk, ident, S), gather_pages(vv, ident, S)
+            ro, _ = window_attention(qq[b, hk][None, :, None], kg[None], vg[None], w.softmax_scale, q_offset=S - 1)
+            ref.append(ro[0, :, 0])
+            got.append(bf16_from_f64(o[b, hk * g:(hk + 1) * g]))
+    got, ref = np.stack(got), np.stack(ref)
+    err = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    print(f"gqa32k decode bf16 rel-L2 {err:.3e}")
+    assert err <= BARS["bf16"]
