@@ -596,11 +596,13 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
   float m_ref = xmax0 > -INFINITY ? ceilf(xmax0) : kRefEmpty;
   bool rescale = false;
 
-  // epilogue: O / l as bfloat16, and the log-sum-exp
-  auto store_out = [&](float l_sum) {
+  // epilogue: O / o_div as bfloat16, and the log-sum-exp of the row sum l_sum (o_div is
+  // l_sum in the units O is accumulated in: they differ when the FP8 V scale is not a power
+  // of two, and the log-sum-exp must not depend on V)
+  auto store_out = [&](float o_div, float l_sum) {
     const int my_q = row_of_lane();
     if (q0 >= Sq || my_q >= Sq) return;
-    const float inv_l = l_sum > 0.0f ? 1.0f / l_sum : 0.0f;  // a row with no key: O = 0, LSE = -inf
+    const float inv_l = l_sum > 0.0f ? 1.0f / o_div : 0.0f;  // a row with no key: O = 0, LSE = -inf
     uint16_t* orow = p.o + (o_row0 + my_q) * C::DV;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
@@ -625,11 +627,16 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
     float rv_o = 1.0f;      // O holds sum(w v) / rv_o
 
     // (the scale is the same in every lane: integer fields of its bits, on the scalar
-    // unit; for a normal float, sv is its biased exponent and rv keeps sign and mantissa)
+    // unit; for a normal float, sv is its biased exponent and rv keeps sign and mantissa.
+    // A subnormal scale m 2^-149 (0 < m < 2^23) takes E8M0 code 0, 2^-127, and rv = m 2^-22
+    // in (0, 2), normalised here with integer operations: exact, and branch-free)
     auto vsplit = [&](float vsc, float& rv, int& sv) {
       const int b = __builtin_amdgcn_readfirstlane(__float_as_int(vsc));
       sv = (b >> 23) & 0xff;
-      rv = __int_as_float((b & (int)0x807fffff) | 0x3f800000);
+      const int mant = b & 0x7fffff;
+      const int top = 31 - __builtin_clz(mant | 1);  // leading bit of a subnormal's mantissa
+      const int sub = (b & (int)0x80000000) | ((top + 105) << 23) | ((mant << (23 - top)) & 0x7fffff);
+      rv = __int_as_float(sv != 0 ? ((b & (int)0x807fffff) | 0x3f800000) : sub);
     };
     // K and V scales of tile t+1 while iteration t runs; the loads for tile t+2 are
     // issued at the top of iteration t, ahead of the tile fills whose wait covers them
@@ -935,8 +942,8 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
 #pragma unroll
     for (int d = 0; d < 4; ++d) pin_acc(oacc[d]);
     pin_acc(rs_acc);
-    // O = oacc * rv_o / l
-    store_out(rs_acc[0] / rv_o);
+    // O = oacc * rv_o / l; the log-sum-exp from l alone
+    store_out(rs_acc[0] / rv_o, rs_acc[0]);
   } else {
     // ===================== BF16: three-stage pipeline =====================
     // Iteration t: PV of tile t-1 (its P formed in iteration t-1), then the maxima of
@@ -1153,7 +1160,8 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
     }
 #pragma unroll
     for (int d = 0; d < 4; ++d) pin_acc(oacc[d]);
-    store_out(sum_across_halves(l_part));
+    const float l_sum = sum_across_halves(l_part);
+    store_out(l_sum, l_sum);
   }
 }
 

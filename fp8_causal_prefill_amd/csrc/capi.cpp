@@ -316,7 +316,9 @@ long long zyfa_attn_decode_workspace_bytes(int B, int Hq, int Dv, int max_kv_len
   const long long parts = decode_splits(max_kv_len, split_keys);
   if (parts <= 1) return 0;
   const long long rows = (long long)B * Hq;
-  if (rows * (2LL * Dv + 4) > (1LL << 60) / parts) return -1;  // (no overflow below)
+  // rows * (2 Dv + 4) * parts <= 2^60, compared in division form so that no product
+  // can overflow (then none below does either)
+  if (rows > ((1LL << 60) / parts) / (2LL * Dv + 4)) return -1;
   const long long o_bytes = (parts * rows * Dv * 2 + 255) / 256 * 256;
   return o_bytes + parts * rows * 4;
 }
@@ -344,7 +346,8 @@ static zyfa_status decode_paged(const void* q, const void* k_cache, const void* 
   const long long parts = decode_splits(max_kv_len, split_keys);
   if (parts * B * Hkv > 0x7FFFFFFFLL) return fail(ZYFA_ERR_UNSUPPORTED, "grid too large");
   const long long need = zyfa_attn_decode_workspace_bytes(B, Hq, Dv, max_kv_len, split_keys);
-  if (need > 0) {
+  if (need < 0) return fail(ZYFA_ERR_UNSUPPORTED, "the splits' partial results would exceed 2^60 bytes");
+  if (parts > 1) {
     if (!workspace || ((uintptr_t)workspace & 255u) != 0)
       return fail(ZYFA_ERR_INVALID_ARGUMENT, "workspace must be non-null and 256-byte aligned");
     if (workspace == (const void*)o || workspace == (const void*)lse || workspace == q || workspace == k_cache ||

@@ -112,11 +112,15 @@ zyfa_status zyfa_quantize_fp8(const void* x, int x_is_bf16, uint8_t* codes, floa
  *
  *   q, k, v      e4m3 codes: q [B, Hq, S, Dqk], k [B, Hkv, S, Dqk], v [B, Hkv, S, Dv].
  *   q_scale      [B, Hq, nb] float32; k_scale, v_scale [B, Hkv, nb] float32; each
- *                finite and > 0. Dequantized input = decode(code) * scale. Any
- *                positive scale is accepted; power-of-two V scales (as written by
- *                zyfa_quantize_fp8) are applied exactly by the matrix instruction,
- *                while the mantissa of other V scales is folded into the
- *                probabilities before their rounding to e4m3.
+ *                finite and > 0 (subnormal floats included). Dequantized input =
+ *                decode(code) * scale. A V scale is split into a power of two, which
+ *                the matrix instruction applies exactly as the V operand's E8M0 scale
+ *                (2^-127 for a subnormal scale), and a factor rv in (0, 2) (1 for the
+ *                power-of-two scales zyfa_quantize_fp8 writes): O is accumulated in
+ *                units of 1 / rv of the latest key tile and multiplied by the ratio
+ *                when rv changes, so the probabilities and their rounding do not
+ *                depend on V. A zero, negative or non-finite scale gives undefined
+ *                output.
  *   scale_block  tokens per scale: 64 or 128.
  *   o            out: [B, Hq, S, Dv] bfloat16 (round-to-nearest-even).
  *   lse          out, may be NULL: [B, Hq, S] float32, natural-log log-sum-exp of

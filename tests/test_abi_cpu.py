@@ -208,6 +208,13 @@ def test_decode_workspace_bytes(lib):
     assert f(4, 8, 128, 256, 256) == 0        # one split: results go straight to o / lse
     assert f(0, 8, 128, 1000, 256) == -1 and f(4, 8, 128, 1000, 0) == -1
     assert f(1 << 30, 1 << 30, 512, 1 << 30, 64) == -1  # would overflow
+    assert f(1 << 30, 1 << 30, 126, 128, 64) == -1  # 2 parts of 2^60 rows: over the limit
+    assert f(1 << 30, 1 << 30, 1 << 30, 1 << 30, 64) == -1
+    # just under the limit: rows * (2 Dv + 4) * parts = 2^60 exactly
+    rows, dv, parts = 1 << 40, 126, 1 << 12
+    assert (2 * dv + 4) * rows * parts == 1 << 60
+    assert f(1 << 20, 1 << 20, dv, parts * 64, 64) == (parts * rows * dv * 2 + 255) // 256 * 256 + parts * rows * 4
+    assert f(1 << 20, (1 << 20) + 1, dv, parts * 64, 64) == -1
 
 
 @pytest.mark.parametrize("kw,expect", [

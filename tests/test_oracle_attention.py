@@ -36,6 +36,35 @@ def test_probability_rows_sum_to_one_and_are_causal():
     assert np.all(p[np.tril_indices(50)] > 0)
 
 
+def _torch_probs(q, k, scale):
+    """Causal softmax by torch's float64 softmax over masked scores (a library routine)."""
+    s = torch.from_numpy(q) @ torch.from_numpy(k).T * scale
+    S = s.shape[0]
+    s = s.masked_fill(torch.ones(S, S, dtype=torch.bool).triu(1), float("-inf"))
+    return torch.softmax(s, dim=-1).numpy(), torch.logsumexp(s, dim=-1).numpy()
+
+
+@pytest.mark.parametrize("scale", [0.3, 1 / math.sqrt(64)])
+def test_probabilities_match_library_softmax_and_attention(scale):
+    # "Error of a Single Attention Call" (ZYFA): P is the causal softmax of scale * Q K^T.
+    # Pinned by torch's softmax of the masked scores, and by P V = the oracle's attention
+    # output (itself pinned by SDPA and brute force below). A dropped or doubled scale
+    # changes P by far more than the tolerance.
+    q, k, v = _qkv(1, 1, 1, 70, 64, 32, seed=11, scale=1.3)
+    q, k, v = q[0, 0], k[0, 0], v[0, 0]
+    p = causal_probs(q, k, scale)
+    pt, lse_t = _torch_probs(q, k, scale)
+    assert np.allclose(p, pt, rtol=1e-12, atol=1e-15)
+    o, lse = causal_attention(q[None, None], k[None, None], v[None, None], scale)
+    assert np.allclose(p @ v, o[0, 0], rtol=0, atol=1e-13)
+    assert np.allclose(lse[0, 0], lse_t, rtol=0, atol=1e-12)
+    # log P_ij + LSE_i is the scaled score of every visible pair
+    i, j = np.tril_indices(70)
+    assert np.allclose(np.log(p[i, j]) + lse[0, 0][i], scale * np.sum(q[i] * k[j], axis=1), rtol=0, atol=1e-11)
+    for wrong in (2 * scale, 1.0):
+        assert not np.allclose(causal_probs(q, k, wrong), pt, rtol=1e-6, atol=1e-9)
+
+
 def test_row0_returns_v0():
     q, k, v = _qkv(2, 4, 2, 33, 128, 128, seed=2)
     o, lse = causal_attention(q, k, v, 1 / math.sqrt(128))

@@ -136,3 +136,64 @@ def test_hadamard_rotation_preserves_scores_and_spreads_outliers():
     e[7] = 1.0
     assert np.allclose(np.abs(hadamard_rotate(e)), 1 / np.sqrt(128))
     assert np.abs(kr).max() < np.abs(k).max() / 3
+
+
+def _torch_decode(codes):
+    """e4m3 values of codes through torch's float8_e4m3fn (a library routine), float64."""
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _varying_scales(B, H, nb, seed):
+    """Scales that differ from block to block: 2^(j mod 5) times a seeded factor in [1, 2)
+    (not only powers of two: the attention entry points accept any positive scale)."""
+    rng = np.random.default_rng(seed)
+    j = np.arange(nb)[None, None, :]
+    return (np.exp2(j % 5) * rng.uniform(1.0, 2.0, (B, H, nb))).astype(np.float32)
+
+
+def _dequantize_rolled(codes, scales, block):
+    """A planted mistake: block j takes block j-1's scale."""
+    return dequantize_blocks(codes, np.roll(scales, 1, axis=2), block)
+
+
+@pytest.mark.parametrize("block,S", [(64, 200), (128, 300), (64, 64), (128, 129)])
+def test_dequantize_applies_each_blocks_own_scale(block, S):
+    # "Error of a Single Attention Call" (ZYFA): the reference attends over the dequantized
+    # inputs the kernel read, element = decode(code) * scale of the element's token block.
+    # Checked element by element against torch's decode of every code, the block found by
+    # explicit division of the token index, the last block ragged (S not a multiple of it).
+    rng = np.random.default_rng(block + S)
+    codes = rng.integers(0, 256, (2, 3, S, 16)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C  # no NaN codes
+    nb = (S + block - 1) // block
+    scales = _varying_scales(2, 3, nb, seed=S)
+    got = dequantize_blocks(codes, scales, block)
+    vals = _torch_decode(codes)
+    want = np.empty_like(vals)
+    for t in range(S):
+        want[:, :, t, :] = vals[:, :, t, :] * scales[:, :, t // block, None].astype(np.float64)
+    assert got.dtype == np.float64 and got.shape == codes.shape
+    assert np.array_equal(got, want)
+    # the same comparison catches a scale taken from the neighbouring block
+    if nb > 1:
+        assert not np.array_equal(_dequantize_rolled(codes, scales, block), want)
+
+
+@pytest.mark.parametrize("block", [64, 128])
+def test_quantize_round_trip_with_block_varying_magnitudes(block):
+    # token block j is scaled by 2^(3 (j mod 5)): each block's scale tracks its own absmax,
+    # and every dequantized element is within e4m3's bound of its own block's scale
+    S = 5 * block + 37
+    x = _x((1, 2, S, 128), seed=block)
+    mag = np.exp2(3.0 * ((np.arange(S) // block) % 5)).astype(np.float32)
+    x = x * mag[None, None, :, None]
+    codes, scales = quantize_blocks(x, block)
+    for j in range(scales.shape[2]):
+        amax = np.abs(x[:, :, j * block:(j + 1) * block]).max(axis=(2, 3)).astype(np.float64)
+        assert np.all(amax / scales[:, :, j] <= 448.0) and np.all(amax / scales[:, :, j] > 224.0)
+    xd = dequantize_blocks(codes, scales, block)
+    s = np.repeat(scales.astype(np.float64), block, axis=2)[:, :, :S, None]
+    assert np.all(np.abs(xd - x) <= np.maximum(np.abs(x) * 2.0 ** -4, s * 2.0 ** -10) * (1 + 1e-5))
+    # a rolled scale puts whole blocks off by a factor of 8 or more
+    xr = _dequantize_rolled(codes, scales, block)
+    assert np.max(np.abs(xr - x) / (np.abs(x) + s)) > 1.0
