@@ -70,10 +70,21 @@ constexpr float kRefEmpty = -1e30f;
 // to 2^-(6 + kPHeadroom) of their block maximum out of it (down to 2^-6 without headroom),
 // while the block maximum stays below 256 and e4m3's largest value, 448.
 constexpr int kPHeadroom = 7;
-// Lean probabilities: code = round(8 y + kLeanBias) for p = 2^y. 56 is the code of 1.0;
-// the linear code overestimates 2^y inside each binade by 0 to 0.69 codes (mean 0.46),
-// and subtracting that mean minimises the error of the normalised output.
-constexpr float kLeanBias = 56.0f - 0.46f;
+// Lean probabilities: the e4m3 code of p = 2^y is close to 8 y + 56 (eight codes per binade,
+// 56 the code of 1.0), but inside each binade 2^y lies below the straight line, by up to 0.69
+// codes. The code is therefore taken on a grid twice as fine, c16 = round(16 y + kLean16Bias),
+// then halved, with the odd half-steps rounded up where the halved code's 3 mantissa bits are
+// 0, 6 or 7 (bit m of kLeanUp), down elsewhere: the thresholds between codes then follow the
+// exponential's curvature. The offset and the table were fitted to the error of the output
+// after normalisation by the rounded row sum, which cancels any common factor of the weights.
+constexpr float kLean16Bias = 110.25f;
+constexpr unsigned kLeanUpLo = 0x00000001u;  // table bytes 0-3 (mantissas 0..3): round up at 0
+constexpr unsigned kLeanUpHi = 0x01010000u;  // table bytes 4-7 (mantissas 4..7): round up at 6, 7
+// The lean codes' values average 0.95917 of the probabilities they code (weighted by the
+// probabilities, over a binade): the row sum that enters the log-sum-exp is divided by it,
+// leaving each code off by at most 0.068 in log (the output, normalised by the same codes'
+// sum, does not depend on a common factor).
+constexpr float kLeanSumScale = 1.0425686f;
 
 template <bool FP8, int DQK, int NWAVES = 8>
 struct Cfg {
@@ -680,18 +691,23 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
     // e4m3 codes of four probabilities p = 2^(s c - bias) of one query row (s: raw
     // scores j0..j0+3 of a 32-key group), packed low byte first. Exact mode: hardware
     // exponential, then round-to-nearest-even conversion. Lean mode ("Lean P: Linear
-    // Approximation of the FP8 Code"): the code of 2^y is close to 8 y + 56 (eight codes
-    // per binade, 56 = 1.0), so it is taken as round-half-even(8 y + kLeanBias) clamped to
-    // [0, 255] (y < kPHeadroom + 1 keeps it at most 120, below e4m3's NaN code 127): one
-    // FMA and one conversion per value instead of an exponential and half a conversion.
+    // Approximation of the FP8 Code"): the code as a linear function of y = s c - bias on
+    // the grid of sixteen steps per binade, round-half-even(16 y + kLean16Bias) clamped to
+    // [0, 255], then halved to e4m3's eight with the mantissa-dependent rounding of the odd
+    // half-steps (a byte lookup of the four codes at once). y < kPHeadroom + 1 keeps the
+    // code at most 119, below e4m3's NaN code 127. Per score: one FMA and one conversion,
+    // plus six integer operations per four scores, instead of an exponential and half a
+    // conversion.
     auto p_codes = [&](const v16f& sv, int j0, float c, float bias) -> int {
       if constexpr (LEAN) {
-        const float c8 = 8.0f * c, b8 = fmaf(-8.0f, bias, kLeanBias);
-        unsigned r = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[j0 + 0], c8, b8), 0, 0u);
-        r = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[j0 + 1], c8, b8), 1, r);
-        r = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[j0 + 2], c8, b8), 2, r);
-        r = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[j0 + 3], c8, b8), 3, r);
-        return (int)r;
+        const float c16 = 16.0f * c, b16 = fmaf(-16.0f, bias, kLean16Bias);
+        unsigned r = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[j0 + 0], c16, b16), 0, 0u);
+        r = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[j0 + 1], c16, b16), 1, r);
+        r = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[j0 + 2], c16, b16), 2, r);
+        r = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[j0 + 3], c16, b16), 3, r);
+        // per byte: (c16 + up[(c16 >> 1) & 7]) >> 1, no carry between bytes (c16 <= 239)
+        const unsigned up = __builtin_amdgcn_perm(kLeanUpHi, kLeanUpLo, (r >> 1) & 0x07070707u);
+        return (int)(((r + up) >> 1) & 0x7F7F7F7Fu);
       } else {
         const float p0 = fast_exp2(fmaf(sv[j0 + 0], c, -bias));
         const float p1 = fast_exp2(fmaf(sv[j0 + 1], c, -bias));
@@ -943,7 +959,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
     for (int d = 0; d < 4; ++d) pin_acc(oacc[d]);
     pin_acc(rs_acc);
     // O = oacc * rv_o / l; the log-sum-exp from l alone
-    store_out(rs_acc[0] / rv_o, rs_acc[0]);
+    store_out(rs_acc[0] / rv_o, LEAN ? rs_acc[0] * kLeanSumScale : rs_acc[0]);
   } else {
     // ===================== BF16: three-stage pipeline =====================
     // Iteration t: PV of tile t-1 (its P formed in iteration t-1), then the maxima of

@@ -152,11 +152,17 @@ zyfa_status zyfa_attn_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t*
  *
  * Same arguments, layouts, scales, errors and output as zyfa_attn_fwd_fp8. Only the
  * probabilities differ: with y = s*c - bias the base-2 exponent of a probability after
- * its block scaling (y < 8), its code is round-half-even(8 y + 55.54) clamped to
- * [0, 255] instead of the round-to-nearest-even e4m3 code of 2^y: one fused multiply-add
- * and one conversion per score, no exponential. The normalisation still uses the sum of
- * exactly these codes' values, so outputs remain weighted averages. An opt-in fast mode:
- * expect about 1.25 times the relative error of zyfa_attn_fwd_fp8.
+ * its block scaling (y < 8), its code is taken from a straight line on a grid of sixteen
+ * steps per binade, c16 = round-half-even(16 y + 110.25) clamped to [0, 255], then halved
+ * to e4m3's eight steps per binade: (c16 + u) >> 1, where u = 1 if the halved code's three
+ * mantissa bits are 0, 6 or 7 and u = 0 otherwise. The rounding up near the binade edges
+ * follows the curvature of 2^y that a straight line of eight steps misses. One fused
+ * multiply-add and one conversion per score plus six integer operations per four scores,
+ * no exponential. The normalisation still uses the sum of exactly these codes' values, so
+ * outputs remain weighted averages and their error is within a few percent of
+ * zyfa_attn_fwd_fp8's (host emulation at 32K Gaussian tokens, late rows: 2.74e-2 against
+ * 2.66e-2; a straight line of eight steps gives 3.08e-2). The codes' values average 0.959
+ * of the probabilities; the log-sum-exp divides that factor out of the row sum.
  */
 zyfa_status zyfa_attn_fwd_fp8_lean(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_scale,
                                    const float* k_scale, const float* v_scale, int scale_block, uint16_t* o,

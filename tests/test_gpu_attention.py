@@ -234,9 +234,10 @@ def test_bf16_short_and_ragged_lengths(S):
 
 # ---- lean probabilities (zyfa_attn_fwd_fp8_lean) ----
 # The linear code adds a bounded, input-independent distortion to every probability, so
-# its error is a fixed multiple of the exact kernel's: the ZYFA page reports 1.22-1.36x;
-# the bar here is 1.5x the exact kernel's error on the same inputs (plus 1e-3 for tiny
-# cases where both are small), and never above 4e-2.
+# its error is a fixed multiple of the exact kernel's: the ZYFA page reports 1.22-1.36x for
+# its straight-line code; the code on the finer grid with mantissa-dependent rounding used
+# here tracks the exponential's curvature. The bar: 1.5x the exact kernel's error on the
+# same inputs (plus 1e-3 for tiny cases where both are small), and never above the FP8 bar.
 LEAN_FACTOR = 1.5
 
 
@@ -253,14 +254,14 @@ def test_fp8_lean_parity(shape):
     print(f"fp8 lean rel-L2 {e_lean:.3e} (exact {e_exact:.3e})")
     assert np.all(np.isfinite(o_lean))
     assert e_lean <= LEAN_FACTOR * e_exact + 1e-3
-    assert e_lean <= 4e-2
+    assert e_lean <= FP8_BAR
     # each weight is off by at most ~1 code (a factor 2^(1/8)); the log-sum-exp moves by less
     assert np.max(np.abs(lse_lean - rlse)) < 0.1
 
 
 def test_fp8_lean_exact_special_cases():
     # V == 1: still exactly 1 (the normalisation uses the same codes); Q == 0: every score
-    # equal, y = 0, code round(55.54) = 56 = 1.0 exactly, so O is the prefix mean of V
+    # equal, so every probability gets the same code and O is the prefix mean of V
     qc, kc, vc, qs, ks, vs = _quantized(1, 4, 2, 600, 128, 64, seed=1)
     ones = torch.full_like(vc, 0x38)
     o, _ = zy.attn_fwd_fp8(qc, kc, ones, qs, ks, torch.ones_like(vs), 64, lean=True)
@@ -300,7 +301,7 @@ def test_rising_scores_move_the_reference(Dqk):
     # weights were subnormal)
     assert e_lean <= min(LEAN_FACTOR * e_exact + 1e-3, FP8_BAR)
     assert np.max(np.abs(lse - rlse)) < 0.062
-    # a lean code of a normal e4m3 value is off by at most 0.083 in log; weights under
+    # a lean code of a normal e4m3 value is off by at most 0.068 in log; weights under
     # 2^-13 of their block's maximum (subnormal) sum to less than 2^-7 of it: < 0.1
     assert np.max(np.abs(lse_lean - rlse)) < 0.1
     ob, lseb = gpu_bf16(q, k, v, scale)

@@ -3,7 +3,7 @@ ABI, against the fp64 oracle on the same inputs.
 
 The oracle is paged_attention with a chunk of one token per sequence (row at position
 kv_len - 1, seeing every key). Bars as for the whole-sequence calls over all outputs:
-BF16 <= 5e-3, FP8 <= 3e-2, lean 4e-2 (the splits' partial outputs are rounded to
+BF16 <= 5e-3, FP8 (exact and lean) <= 3e-2 (the splits' partial outputs are rounded to
 bfloat16 before the merge, which adds at most about one bfloat16 rounding). Beyond the
 bars: with one split and BF16 inputs, decode equals the paged prefill call with a
 one-token chunk per sequence, bit for bit (both take the same tiles in the same order for
@@ -24,7 +24,7 @@ from workloads import custom, generate, page_table, scatter_pages
 
 pytestmark = pytest.mark.gpu
 
-BARS = {"fp8": 3e-2, "lean": 4e-2, "bf16": 5e-3}
+BARS = {"fp8": 3e-2, "lean": 3e-2, "bf16": 5e-3}
 
 
 def _case(*a):

@@ -33,7 +33,7 @@ from workloads import custom, generate, page_table, scatter_pages
 
 pytestmark = pytest.mark.gpu
 
-BARS = {"fp8": 3e-2, "lean": 4e-2}
+BARS = {"fp8": 3e-2, "lean": 3e-2}
 MODES = ["fp8", "lean"]
 
 
@@ -43,7 +43,7 @@ def _case(*a):
 
 def _lse_ok(mode, got, ref):
     # exact: a probability's e4m3 rounding moves the row sum by at most a factor 1 + 2^-4;
-    # lean: a code in e4m3's normal range is off by at most 0.083 in log, and the weights
+    # lean: a code in e4m3's normal range is off by at most 0.068 in log, and the weights
     # under 2^-13 of their block maximum add less than 2^-7 of it
     d = np.abs(got - ref)
     return d.max() < (math.log(1 + 2 ** -4) if mode == "fp8" else 0.1)

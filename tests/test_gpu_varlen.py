@@ -2,7 +2,7 @@
 against the fp64 oracle on the same inputs.
 
 Bars as for the whole-sequence calls (relative L2 over the tokens of all sequences:
-BF16 <= 5e-3, FP8 <= 3e-2, lean 4e-2). Beyond the bars: the real tokens of a sequence
+BF16 <= 5e-3, FP8 <= 3e-2, exact and lean). Beyond the bars: the real tokens of a sequence
 padded at its end match the oracle on the unpadded sequence; every sequence equals a plain
 call on that sequence alone bit for bit (same codes and scales); tokens after the last
 sequence keep what the output held; a sequence whose cu_seqlens entries break the rules is
@@ -22,7 +22,7 @@ from workloads import custom, generate
 
 pytestmark = pytest.mark.gpu
 
-BARS = {"fp8": 3e-2, "lean": 4e-2, "bf16": 5e-3}
+BARS = {"fp8": 3e-2, "lean": 3e-2, "bf16": 5e-3}
 SENTINEL = 7.0
 
 

@@ -17,6 +17,13 @@ It pins the reason the e5m2 and FP4 variants are not built: on Gaussian inputs t
 e4m3 code stays within the FP8 bar of 3e-2 (P's share only), e5m2 lands at about twice
 the exact-P error, above the bar, and FP4's three and a half binades per block drop most
 of the softmax mass (relative L2 near 0.5).
+
+The last two tests pin the lean code the FP8 kernel uses ("Lean P: Linear Approximation of
+the FP8 Code", refined): a straight line on a sixteen-step grid halved to e4m3 with
+mantissa-dependent rounding. Emulated with the kernel's integer reference and block
+scaling, it stays within 10 % of exactly rounded probabilities on rows that see many keys,
+where the straight eight-step line is 20 % worse; its range and the mean factor the kernel
+divides out of the log-sum-exp's row sum are checked directly.
 """
 
 import math
@@ -88,3 +95,81 @@ def test_lean_codes_in_other_formats():
     assert err["exact"] < err["e4m3"] < 3e-2
     assert 3e-2 < err["e5m2"] < 2.5 * err["exact"] + 1e-2
     assert err["e2m1"] > 0.3
+
+
+# ---- the lean code the FP8 kernel uses (zyfa_attn_fwd_fp8_lean) ----
+# A straight line on a grid of sixteen steps per binade, halved to e4m3's eight with the
+# odd half-steps rounded up where the halved code's mantissa is 0, 6 or 7 (the kernel's
+# kLean16Bias and its kLeanUpLo / kLeanUpHi byte table).
+LEAN16_BIAS = 110.25
+LEAN16_UP = np.array([1, 0, 0, 0, 0, 0, 1, 1])
+
+
+def _lean16_codes(y):
+    c16 = np.clip(np.rint(16.0 * y + LEAN16_BIAS), 0, 255).astype(np.int64)
+    return (c16 + LEAN16_UP[(c16 >> 1) & 7]) >> 1
+
+
+def _attention_kernel_codes(q, k, v, scale, mode):
+    """Causal attention with probabilities coded as the FP8 kernel does: integer reference
+    ceil(row max), block exponent floor(block max - reference) - 7 (block maximum in
+    [2^7, 2^8)), codes by `mode` ("exact": e4m3 rounding of the exponential; "line": the
+    straight eight-step line; "lean16": the kernel's lean code), each row normalised by the
+    sum of the coded values."""
+    S = q.shape[0]
+    s = (q @ k.T) * scale / math.log(2.0)
+    out = np.zeros((S, v.shape[1]))
+    c0 = E4M3["one"] - E4M3["step"] * (0.5 - (1 / math.log(2.0) - 1))
+    for i in range(S):
+        row = s[i, :i + 1]
+        ref = math.ceil(row.max())
+        p = np.zeros(i + 1)
+        for b0 in range(0, i + 1, 64):
+            blk = row[b0:b0 + 64]
+            e = math.floor(blk.max() - ref) - 7
+            y = blk - ref - e
+            if mode == "exact":
+                val = _e4m3_round(2.0 ** y)
+            elif mode == "line":
+                val = _decode(E4M3, np.clip(np.rint(8.0 * y + c0), 0, 126))
+            else:
+                val = _decode(E4M3, _lean16_codes(y))
+            p[b0:b0 + 64] = val * 2.0 ** e
+        out[i] = p @ v[:i + 1] / p.sum()
+    return out
+
+
+def test_kernel_lean_code_tracks_exact_rounding():
+    # On spread-out (Gaussian) attention the error of normalised attention is the spread of
+    # the per-weight coding error. Over rows that see many keys the sixteen-step code with
+    # the curvature table stays within 10 % of exactly rounded probabilities and well under
+    # the straight eight-step line, whose late rows exceed the FP8 bar at 32K tokens.
+    rng = np.random.default_rng([4242, 1])
+    S, D = 2048, 128
+    q, k, v = (rng.standard_normal((S, D)) for _ in range(3))
+    scale = 1 / math.sqrt(D)
+    rows = np.arange(1024, S, 16)
+    ref = causal_attention(q[None, None], k[None, None], v[None, None], scale, rows=rows)[0][0, 0]
+    err = {}
+    for mode in ("exact", "line", "lean16"):
+        o = _attention_kernel_codes(q[:S], k, v, scale, mode)[rows]
+        err[mode] = float(np.sqrt(np.mean(np.sum((o - ref) ** 2, 1) / np.sum(ref ** 2, 1))))
+    print(err)
+    assert err["lean16"] <= 1.1 * err["exact"] and err["lean16"] < 0.95 * err["line"]
+
+
+def test_kernel_lean_code_range_and_mean_factor():
+    # every code the block scaling can produce (y < 8) is a finite e4m3 value below NaN 127,
+    # each normal-range code is within e^(+-0.07) of its probability times their mean factor; the codes' values
+    # average 0.95917 of the probabilities over a binade (weighted by the probability): the
+    # factor the kernel divides out of the row sum for the log-sum-exp (kLeanSumScale)
+    y = np.linspace(-13.0, 8.0 - 1e-9, 1_000_001)
+    c = _lean16_codes(y)
+    assert c.max() == 119 and c.min() == 0
+    normal = y >= -5.5  # codes of e4m3's normal binades (its subnormals start at 2^-6)
+    val = _decode(E4M3, c[normal])
+    assert np.max(np.abs(np.log(val / np.exp2(y[normal])) - math.log(0.95917))) < 0.07
+    f = (np.arange(1 << 20) + 0.5) / (1 << 20) + 3.0
+    w = np.exp2(f)
+    mean = np.sum(_decode(E4M3, _lean16_codes(f))) / np.sum(w)
+    assert abs(mean - 0.95917) < 2e-5 and abs(1.0 / mean - 1.0425686) < 2e-5
