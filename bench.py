@@ -21,7 +21,12 @@ computed also give a full-size parity figure (``sampled_rel_l2_fp8``).
 ``sustained`` runs each headline kernel back to back for a few seconds after the clock
 has settled and reports, next to its time, the median shader clock, the socket power,
 the energy per call and the fraction of the window the board spent at its power limit
-(amdsmi telemetry; null with the reason when the driver does not provide it).
+(amdsmi telemetry; null with the reason when the driver does not provide it); its
+``structured_inputs`` part does the same for the FP8 kernels at the 16K activation-like
+shape on Gaussian, activation-like (with and without rotation) and rising-score inputs.
+The activation-like workload's record in ``other_workloads`` carries, besides times, its
+error figures with and without rotation (kernel against the oracle on the codes it read,
+input quantization against unquantized inputs), computed in the CPU leg.
 """
 
 import argparse
@@ -77,6 +82,18 @@ def time_loop(fn, steps, warmup, torch):
     return (time.perf_counter() - t0) / steps
 
 
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, q, k, v, target_s=15.0):
     """Time the fp64 oracle on a bounded sample of the workload: whole query heads
     (quantize + dequantize the head's Q and its KV head, then causal attention over
@@ -85,9 +102,11 @@ def cpu_baseline(w, q, k, v, target_s=15.0):
     from oracle import causal_attention, dequantize_blocks, quantize_blocks
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
-        cores = 1
+        blas_threads = 1
+    available = len(os.sched_getaffinity(0))
+    cores = min(blas_threads, available)  # the threads the oracle's BLAS calls actually run on
     group = w.Hq // w.Hkv
     refs = {}
     flops = 0.0
@@ -103,6 +122,7 @@ def cpu_baseline(w, q, k, v, target_s=15.0):
             break
     secs = time.perf_counter() - t0
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "host_cores_available": available, "blas_threads": int(blas_threads), "cpu_model": cpu_model(),
             "sample": f"fp64 oracle on {len(refs)} of {w.B * w.Hq} query heads of the same workload (batch 0, "
                       f"heads 0..{len(refs) - 1}, all {w.S} rows each: quantize, dequantize, causal attention); "
                       f"{secs:.1f} s",
@@ -226,6 +246,43 @@ def sustained(tel, fn, flops, peak, settle_s, window_s, stream, torch):
             rec["power_limited_fraction"] = (b["ppt"] - a["ppt"]) / (b["acc"] - a["acc"])
             if a["thm"] is not None and b["thm"] is not None:
                 rec["thermal_limited_fraction"] = (b["thm"] - a["thm"]) / (b["acc"] - a["acc"])
+    return rec
+
+
+def structured_sustained(tel, window_s, stream, torch, zy):
+    """The sustained-clock measurement on inputs of different structure at one shape, the
+    activation-like workload's (B=1, Hq=32, Hkv=8, S=16384, D=128): Gaussian inputs, the
+    activation-like inputs without and with the 128-point rotation of Q and K, and rising
+    scores (the lazy reference keeps moving). ZYFA, "Dependence of the Shader Clock on
+    Operand Values" and "Throughput on Captured Activations at Sustained Clocks": the clock
+    the board holds depends on the operands, so the same kernel is measured on each. FP8
+    exact on every input set, lean on the Gaussian and rotated activation-like ones."""
+    from workloads import WORKLOADS, custom, generate
+    act = WORKLOADS["act16k"]
+    shape = dict(B=act.B, Hq=act.Hq, Hkv=act.Hkv, S=act.S, Dqk=act.Dqk, Dv=act.Dv, scale_block=act.scale_block)
+    sets = [("gaussian", custom(**shape, wid=960), False), ("activation", act, False),
+            ("activation_hadamard", act, True), ("rising", custom(**shape, dist="rising", wid=961), False)]
+    dev = torch.device("cuda:0")
+    rec = {"shape": f"B={act.B} Hq={act.Hq} Hkv={act.Hkv} S={act.S} D={act.Dqk}", "settle_s": 1.5,
+           "window_s": window_s}
+    o = torch.empty((act.B, act.Hq, act.S, act.Dv), dtype=torch.bfloat16, device=dev)
+    for name, w, had in sets:
+        q, k, v = generate(w, seed=0)
+        qc, qs = zy.quantize_fp8(torch.from_numpy(q).to(dev), w.scale_block, had)
+        kc, ks = zy.quantize_fp8(torch.from_numpy(k).to(dev), w.scale_block, had)
+        vc, vs = zy.quantize_fp8(torch.from_numpy(v).to(dev), w.scale_block, False)
+        del q, k, v
+        for lean in ((False, True) if name in ("gaussian", "activation_hadamard") else (False,)):
+            key = name + ("_fp8_lean" if lean else "_fp8")
+            r = sustained(tel, lambda: zy.attn_fwd_fp8(qc, kc, vc, qs, ks, vs, w.scale_block, w.softmax_scale, o=o,
+                                                       lean=lean), w.flops, PEAK_FP8, 1.5, window_s, stream, torch)
+            rec[key] = r
+            print(f"[bench] sustained 16K {key}: {r['ms']:.3f} ms, {r['frac'] * 100:.1f}% of peak, clock "
+                  f"{r['gfxclk_mhz_median']} MHz, power {r.get('socket_power_w')} W, "
+                  f"{r.get('energy_per_call_j')} J/call", file=sys.stderr, flush=True)
+        del qc, kc, vc
+    del o
+    torch.cuda.empty_cache()
     return rec
 
 
@@ -420,18 +477,30 @@ def decode_batch(w, kc, vc, ks, vs, kd, vd, steps, warmup, stream, torch, zy):
     return rec
 
 
+ERROR_HEADS = (0, 13)  # query heads whose sampled rows give the activation-like error figures
+ERROR_ROWS = 256
+
+
 def other_workloads(names, steps, warmup, torch, zy):
     """Kernel throughput on the other benchmark shapes (4K MHA, 32K MLA, 16K activation-like
     with and without the Hadamard rotation of Q and K): FP8 exact and lean, and BF16.
-    Reported from the median launch time (these shorter runs see occasional outliers)."""
-    from workloads import WORKLOADS, generate
-    out = {}
+    Reported from the median launch time (these shorter runs see occasional outliers).
+    For the activation-like shape also returns, per rotation setting, what the CPU leg needs
+    for its error figures: the float32 inputs, the codes and scales the kernel read and the
+    kernel's outputs, for ERROR_ROWS sampled rows of the ERROR_HEADS query heads."""
+    from workloads import WORKLOADS, generate, sample_rows
+    out, samples = {}, {}
     stream = torch.cuda.current_stream()
     for name in names:
         w = WORKLOADS[name]
         q, k, v = generate(w, seed=0)
         dev = torch.device("cuda:0")
         qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+        if w.dist == "activation":
+            group = w.Hq // w.Hkv
+            rows = sample_rows(w.S, ERROR_ROWS, seed=1)
+            samples[name] = {"w": w, "rows": rows, "heads": ERROR_HEADS,
+                             "inputs": {h: (q[0, h], k[0, h // group], v[0, h // group]) for h in ERROR_HEADS}}
         del q, k, v
         rec = {"shape": f"B={w.B} Hq={w.Hq} Hkv={w.Hkv} S={w.S} Dqk={w.Dqk} Dv={w.Dv}", "flops": w.flops}
         # the Q quantization pass, without and with the Hadamard rotation (HBM-bound: 4 bytes
@@ -453,6 +522,14 @@ def other_workloads(names, steps, warmup, torch, zy):
                                                               o=o, lean=lean), steps, warmup, stream, torch)
                 rec[mode + tag] = {"ms_mean": ms, "ms": med, "tflops": w.flops / med / 1e9,
                                    "frac_of_fp8_peak": w.flops / med / 1e9 / PEAK_FP8}
+                if name in samples:
+                    sm = samples[name].setdefault(had, {})
+                    idx = torch.from_numpy(samples[name]["rows"]).to(dev)
+                    for h in ERROR_HEADS:
+                        g = h // (w.Hq // w.Hkv)
+                        sm.setdefault(h, {"codes": tuple(t[0, hh].cpu().numpy() for t, hh in
+                                                         ((qc, h), (qs, h), (kc, g), (ks, g), (vc, g), (vs, g)))})
+                        sm[h][mode] = o[0, h].index_select(0, idx).float().cpu().numpy().astype(np.float64)
             del qc, kc, vc
         qb, kb, vb = qd.to(torch.bfloat16), kd.to(torch.bfloat16), vd.to(torch.bfloat16)
         ob = torch.empty((w.B, w.Hq, w.S, w.Dv), dtype=torch.bfloat16, device=dev)
@@ -464,6 +541,49 @@ def other_workloads(names, steps, warmup, torch, zy):
               f"bf16 {rec['bf16']['ms']:.3f} ms", file=sys.stderr, flush=True)
         del qd, kd, vd, qb, kb, vb, o, ob
         torch.cuda.empty_cache()
+    return out, samples
+
+
+def activation_errors(sample):
+    """Error figures of the activation-like workload (ZYFA, "FP8 Error in Full-Model
+    Inference": the rotation of Q and K roughly halves the error that input quantization
+    adds), from the sampled rows other_workloads kept, per rotation setting:
+
+    * kernel_rel_l2_fp8 / _lean: the kernel against the fp64 oracle on the codes and scales
+      it read (the parity figure);
+    * input_quantization_rel_l2: the oracle on those dequantized inputs against fp64
+      attention on the unquantized float32 inputs (the rotation is orthonormal, so the
+      unrotated inputs give the same scores);
+    * end_to_end_rel_l2_fp8 / _lean: the kernel against attention on the unquantized inputs.
+
+    Runs the oracle, so it belongs to the CPU leg."""
+    from oracle import causal_attention, dequantize_blocks
+    w, rows, heads = sample["w"], sample["rows"], sample["heads"]
+    blk = w.scale_block
+    rel = lambda a, b: float(np.sqrt(np.sum((a - b) ** 2) / np.sum(b ** 2)))
+    exact = {}
+    for h in heads:
+        qh, kh, vh = sample["inputs"][h]
+        exact[h] = causal_attention(qh[None, None], kh[None, None], vh[None, None], w.softmax_scale, rows=rows)[0][0, 0]
+    out = {"rows_per_head": len(rows), "heads": list(heads)}
+    for had in (False, True):
+        sm = sample.get(had)
+        if sm is None:
+            continue
+        refs, got = {}, {"fp8": {}, "fp8_lean": {}}
+        for h in heads:
+            qc, qs, kc, ks, vc, vs = sm[h]["codes"]
+            deq = [dequantize_blocks(c[None, None], sc[None, None], blk) for c, sc in ((qc, qs), (kc, ks), (vc, vs))]
+            refs[h] = causal_attention(*deq, w.softmax_scale, rows=rows)[0][0, 0]
+            for mode in got:
+                got[mode][h] = sm[h][mode]
+        cat = lambda d: np.concatenate([d[h] for h in heads])
+        ref_q, ref_x = cat(refs), cat(exact)
+        out["hadamard" if had else "no_rotation"] = {
+            "kernel_rel_l2_fp8": rel(cat(got["fp8"]), ref_q), "kernel_rel_l2_fp8_lean": rel(cat(got["fp8_lean"]), ref_q),
+            "input_quantization_rel_l2": rel(ref_q, ref_x),
+            "end_to_end_rel_l2_fp8": rel(cat(got["fp8"]), ref_x),
+            "end_to_end_rel_l2_fp8_lean": rel(cat(got["fp8_lean"]), ref_x)}
     return out
 
 
@@ -630,6 +750,8 @@ def main():
                 print(f"[bench] sustained {name}: {r['ms']:.3f} ms, {r['frac'] * 100:.1f}% of peak, "
                       f"clock {r['gfxclk_mhz_median']} MHz, power {r.get('socket_power_w')} W", file=sys.stderr,
                       flush=True)
+            if not args.no_others:
+                sustained_rec["structured_inputs"] = structured_sustained(tel, args.sustain, stream, torch, zy)
 
     achieved = flops / attn_s / 1e12
     line = {
@@ -670,9 +792,15 @@ def main():
 
     if not args.no_others:
         others = [n for n in ("mha4k", "mla32k", "act16k") if n != w.name]
-        line["other_workloads"] = other_workloads(others, max(args.steps // 5, 5), max(args.warmup // 10, 5), torch, zy)
+        line["other_workloads"], error_samples = other_workloads(others, max(args.steps // 5, 5),
+                                                                 max(args.warmup // 10, 5), torch, zy)
 
     if not args.no_cpu:
+        for name, sample in (error_samples if not args.no_others else {}).items():
+            t0 = time.perf_counter()
+            line["other_workloads"][name]["error"] = activation_errors(sample)
+            print(f"[bench] {name} error figures ({time.perf_counter() - t0:.1f} s): "
+                  f"{json.dumps(line['other_workloads'][name]['error'])}", file=sys.stderr, flush=True)
         cpu, refs = cpu_baseline(w, q, k, v)
         # the sampled heads also give a full-size parity figure for the timed configuration
         num = den = 0.0

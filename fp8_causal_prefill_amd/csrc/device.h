@@ -159,18 +159,23 @@ __device__ __forceinline__ void wait_vmem() {
 }
 
 // The value of lane l ^ M, for M in {1, 2, 4, 8, 16}, without a trip through the LDS
-// crossbar (which __shfl_xor takes): M = 1, 2 are DPP quad permutations; M = 4, 8 pick a
-// DPP row shift down or up by M (within each 16-lane row) by the lane's bit M; M = 16 swaps
+// crossbar (which __shfl_xor takes): M = 1, 2 are DPP quad permutations; M = 8 is a DPP
+// rotation of each 16-lane row by 8 lanes (which is l ^ 8 within the row); M = 4 picks a
+// DPP row shift down or up by 4 by the lane's bit 2 (two moves and a select); M = 16 swaps
 // the odd 16-lane rows of one copy with the even rows of another (v_permlane16_swap) and
 // takes, per row, the copy that holds the partner row.
 template <int M>
 __device__ __forceinline__ float lane_xor(float v) {
   const int x = __builtin_bit_cast(int, v);
+  // (every lane's source lane exists for these patterns, so the bound-control form, which
+  // needs no copy of the old value in the destination, gives the same result)
   if constexpr (M == 1) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
   } else if constexpr (M == 2) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
-  } else if constexpr (M == 4 || M == 8) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true));  // quad_perm 2,3,0,1
+  } else if constexpr (M == 8) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true));  // row_ror:8
+  } else if constexpr (M == 4) {
     const int up = __builtin_amdgcn_update_dpp(x, x, 0x100 + M, 0xF, 0xF, false);    // row_shl: lane l + M
     const int down = __builtin_amdgcn_update_dpp(x, x, 0x110 + M, 0xF, 0xF, false);  // row_shr: lane l - M
     return __builtin_bit_cast(float, (__lane_id() & M) ? down : up);
@@ -180,6 +185,15 @@ __device__ __forceinline__ float lane_xor(float v) {
     // r[0]: rows (0, 0, 2, 2) of x; r[1]: rows (1, 1, 3, 3)
     return __builtin_bit_cast(float, (__lane_id() & 16) ? r[0] : r[1]);
   }
+}
+
+// The value of lane l ^ M for M < 32 through ds_swizzle_b32 (bit mode: and-mask 31, xor-mask
+// M, within each group of 32 lanes): the LDS crossbar moves it, no vector ALU instruction
+// and no LDS memory access; the result comes back through the LDS queue (lgkmcnt).
+template <int M>
+__device__ __forceinline__ float lane_xor_swizzle(float v) {
+  static_assert(M > 0 && M < 32, "swizzle xor stays within 32 lanes");
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x1F | (M << 10)));
 }
 
 // max of a value across lanes i and i+32.

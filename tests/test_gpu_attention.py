@@ -72,15 +72,25 @@ def test_fp8_parity(shape):
 
 
 def test_fp8_activation_like_with_and_without_rotation():
+    # parity against the oracle on the codes the kernel read, with and without the 128-point
+    # rotation; against attention on the unquantized inputs the rotation must cut the error
+    # that input quantization adds ("FP8 Error in Full-Model Inference": rotating Q and K
+    # spreads the outlier channels and roughly halves the input error)
     w = custom(1, 8, 2, 700, 128, 128, dist="activation", scale_block=128, wid=700)
     q, k, v = generate(w, seed=0)
+    exact, _ = causal_attention(q, k, v, w.softmax_scale)
+    errs = {}
     for hadamard in (False, True):
         _case("act", hadamard=hadamard)
         o, _, parts = gpu_fp8(q, k, v, 128, hadamard=hadamard)
         ro, _ = oracle_attention_from_codes(parts, 128, w.softmax_scale)
         err = rel_l2(o, ro)
-        print(f"fp8 act hadamard={hadamard} rel-L2 {err:.3e}")
+        errs[hadamard] = (rel_l2(ro, exact), rel_l2(o, exact))
+        print(f"fp8 act hadamard={hadamard} rel-L2 {err:.3e}; vs unquantized inputs: oracle on the codes "
+              f"{errs[hadamard][0]:.3e}, kernel {errs[hadamard][1]:.3e}")
         assert err <= FP8_BAR
+    assert errs[True][0] < 0.6 * errs[False][0]  # input-quantization error alone
+    assert errs[True][1] < 0.6 * errs[False][1]  # end to end
 
 
 def test_fp8_mla_activation_like_with_and_without_rotation():
