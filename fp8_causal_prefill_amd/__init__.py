@@ -461,6 +461,60 @@ def attn_decode_fp8_paged(q, k_cache, v_cache, q_scale, k_cache_scale, v_cache_s
     return o, lse
 
 
+NOALLOC_SCRATCH_BYTES = 8 << 20  # the library's per-GPU scratch array for the allocation-free decode
+
+
+def attn_decode_fp8_paged_noalloc(q, k_cache, v_cache, q_scale, k_cache_scale, v_cache_scale, scale_block: int,
+                                  kv_lens, block_table, max_kv_len: int, o, lse=None, softmax_scale=None,
+                                  split_keys=None, lean: bool = False):
+    """attn_decode_fp8_paged for callers that cannot allocate (graph capture, tight serving
+    loops): the splits' partial results go to the library's per-GPU scratch array, and this
+    wrapper allocates nothing either, so the caller passes o [B, Hq, Dv] bfloat16 and, if
+    wanted, lse [B, Hq] float32. Calls that overlap on one GPU race. Returns (o, lse)."""
+    if o is None:
+        raise ValueError("the allocation-free decode writes into a caller's o")
+    B, Hq, Dqk = q.shape
+    num_pages, Hkv, page_size, Dk = k_cache.shape
+    if Dk != Dqk or tuple(v_cache.shape[:3]) != (num_pages, Hkv, page_size):
+        raise ValueError(f"inconsistent shapes q {tuple(q.shape)} k_cache {tuple(k_cache.shape)} "
+                         f"v_cache {tuple(v_cache.shape)}")
+    pq = _dev(q, "q", torch.uint8, 3)
+    pk = _dev(k_cache, "k_cache", torch.uint8, 4)
+    pv = _dev(v_cache, "v_cache", torch.uint8, 4)
+    pkl = _dev(kv_lens, "kv_lens", torch.int32, 1)
+    pbt = _dev(block_table, "block_table", torch.int32, 2)
+    if kv_lens.shape[0] != B or block_table.shape[0] != B:
+        raise ValueError("kv_lens and block_table need one entry / row per sequence")
+    Dv = v_cache.shape[3]
+    po = _dev(o, "o", torch.bfloat16, 3)
+    if tuple(o.shape) != (B, Hq, Dv):
+        raise ValueError("o has the wrong shape")
+    plse = None
+    if lse is not None:
+        plse = _dev(lse, "lse", torch.float32, 2)
+        if tuple(lse.shape) != (B, Hq):
+            raise ValueError("lse has the wrong shape")
+    if split_keys is None:
+        split_keys = decode_split_keys(B, Hkv, int(max_kv_len), 1024 if Hq <= 32 * Hkv else 256)
+    g = Hq // Hkv if Hkv > 0 else 0
+    nbg = (g + scale_block - 1) // scale_block if scale_block > 0 else 0
+    nbp = page_size // scale_block if scale_block > 0 else 0
+    psq = _dev(q_scale, "q_scale", torch.float32, 3)
+    psk = _dev(k_cache_scale, "k_cache_scale", torch.float32, 3)
+    psv = _dev(v_cache_scale, "v_cache_scale", torch.float32, 3)
+    if (tuple(q_scale.shape) != (B, Hkv, nbg) or tuple(k_cache_scale.shape) != (num_pages, Hkv, nbp)
+            or tuple(v_cache_scale.shape) != (num_pages, Hkv, nbp)):
+        raise ValueError("scale tensors have the wrong shape")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(Dqk)
+    st = load().zyfa_attn_decode_fp8_paged_noalloc(pq, pk, pv, psq, psk, psv, scale_block, po, plse, pkl, pbt, B,
+                                                   int(max_kv_len), block_table.shape[1], num_pages, page_size, Hq,
+                                                   Hkv, Dqk, Dv, float(softmax_scale), int(split_keys),
+                                                   int(bool(lean)), _stream())
+    _lib.check(st, "zyfa_attn_decode_fp8_paged_noalloc")
+    return o, lse
+
+
 def attn_decode_bf16_paged(q, k_cache, v_cache, kv_lens, block_table, max_kv_len: int, softmax_scale=None,
                            split_keys=None, o=None, lse=None, return_lse: bool = False):
     """attn_decode_fp8_paged on bfloat16 tensors. Returns (o bfloat16 [B, Hq, Dv], lse or None)."""

@@ -36,6 +36,7 @@ _SIGNATURES = {
     "zyfa_attn_decode_fp8_paged": ([_vp] * 6 + [_i] + [_vp] * 4 + [_i] * 9 + [_f, _i, _vp, ctypes.c_longlong, _i, _vp],
                                    _i),
     "zyfa_attn_decode_bf16_paged": ([_vp] * 7 + [_i] * 9 + [_f, _i, _vp, ctypes.c_longlong, _vp], _i),
+    "zyfa_attn_decode_fp8_paged_noalloc": ([_vp] * 6 + [_i] + [_vp] * 4 + [_i] * 9 + [_f, _i, _i, _vp], _i),
 }
 
 

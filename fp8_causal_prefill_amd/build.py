@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libzyfa.so")
-SOURCES = ["capi.cpp", "attn_fwd.hip", "quantize.hip", "merge.hip"]
+SOURCES = ["capi.cpp", "attn_fwd.hip", "quantize.hip", "merge.hip", "scratch.hip"]
 ARCH = "gfx950"
 
 

@@ -331,7 +331,7 @@ static zyfa_status decode_paged(const void* q, const void* k_cache, const void* 
                                 float* lse, const int* kv_lens, const int* block_table, int B, int max_kv_len,
                                 int max_pages, int num_pages, int page_size, int Hq, int Hkv, int Dqk, int Dv,
                                 float softmax_scale, int split_keys, void* workspace, long long workspace_bytes,
-                                bool fp8, bool lean, void* stream) {
+                                bool fp8, bool lean, void* stream, bool use_scratch = false) {
   zyfa_status st = check_attn_common(q, k_cache, v_cache, o, lse, B, Hq, Hkv, 1, 1, 0, 0, 1, Dqk, Dv, softmax_scale);
   if (st != ZYFA_OK) return st;
   st = check_paged(k_cache, v_cache, kv_lens, block_table, B, max_pages, num_pages, page_size, Hkv, Dqk, Dv);
@@ -347,7 +347,16 @@ static zyfa_status decode_paged(const void* q, const void* k_cache, const void* 
   if (parts * B * Hkv > 0x7FFFFFFFLL) return fail(ZYFA_ERR_UNSUPPORTED, "grid too large");
   const long long need = zyfa_attn_decode_workspace_bytes(B, Hq, Dv, max_kv_len, split_keys);
   if (need < 0) return fail(ZYFA_ERR_UNSUPPORTED, "the splits' partial results would exceed 2^60 bytes");
-  if (parts > 1) {
+  if (use_scratch) {
+    // the allocation-free entry point: the partial results go to the library's per-GPU
+    // scratch array (none is needed with one split)
+    if (need > (long long)zyfa::kScratchBytes)
+      return fail(ZYFA_ERR_UNSUPPORTED,
+                  "the splits' partial results need %lld bytes; the allocation-free decode holds %lld (use larger "
+                  "split_keys, or zyfa_attn_decode_fp8_paged with a workspace)",
+                  need, (long long)zyfa::kScratchBytes);
+    workspace = nullptr;  // (looked up once every argument has passed its checks)
+  } else if (parts > 1) {
     if (!workspace || ((uintptr_t)workspace & 255u) != 0)
       return fail(ZYFA_ERR_INVALID_ARGUMENT, "workspace must be non-null and 256-byte aligned");
     if (workspace == (const void*)o || workspace == (const void*)lse || workspace == q || workspace == k_cache ||
@@ -366,6 +375,11 @@ static zyfa_status decode_paged(const void* q, const void* k_cache, const void* 
     if (page_size % scale_block != 0)
       return fail(ZYFA_ERR_INVALID_ARGUMENT, "page_size (%d) must be a multiple of scale_block (%d)", page_size,
                   scale_block);
+  }
+  if (use_scratch && parts > 1) {
+    const hipError_t e = zyfa::scratch_of_current_device(&workspace);
+    if (e != hipSuccess || workspace == nullptr)
+      return fail(ZYFA_ERR_LAUNCH, "device scratch lookup failed: %s", hipGetErrorString(e));
   }
   const long long rows = (long long)B * Hq;
   uint16_t* o_parts = parts > 1 ? (uint16_t*)workspace : o;
@@ -404,6 +418,18 @@ zyfa_status zyfa_attn_decode_fp8_paged(const uint8_t* q, const uint8_t* k_cache,
   return decode_paged(q, k_cache, v_cache, q_scale, k_cache_scale, v_cache_scale, scale_block, o, lse, kv_lens,
                       block_table, B, max_kv_len, max_pages, num_pages, page_size, Hq, Hkv, Dqk, Dv, softmax_scale,
                       split_keys, workspace, workspace_bytes, true, lean == 1, stream);
+}
+
+zyfa_status zyfa_attn_decode_fp8_paged_noalloc(const uint8_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                               const float* q_scale, const float* k_cache_scale,
+                                               const float* v_cache_scale, int scale_block, uint16_t* o, float* lse,
+                                               const int* kv_lens, const int* block_table, int B, int max_kv_len,
+                                               int max_pages, int num_pages, int page_size, int Hq, int Hkv, int Dqk,
+                                               int Dv, float softmax_scale, int split_keys, int lean, void* stream) {
+  if (lean != 0 && lean != 1) return fail(ZYFA_ERR_INVALID_ARGUMENT, "lean must be 0 or 1");
+  return decode_paged(q, k_cache, v_cache, q_scale, k_cache_scale, v_cache_scale, scale_block, o, lse, kv_lens,
+                      block_table, B, max_kv_len, max_pages, num_pages, page_size, Hq, Hkv, Dqk, Dv, softmax_scale,
+                      split_keys, nullptr, 0, true, lean == 1, stream, /*use_scratch=*/true);
 }
 
 zyfa_status zyfa_attn_decode_bf16_paged(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define ZYFA_ABI_VERSION 5
+#define ZYFA_ABI_VERSION 6
 
 typedef enum zyfa_status {
   ZYFA_OK = 0,
@@ -359,6 +359,33 @@ zyfa_status zyfa_attn_decode_fp8_paged(const uint8_t* q, const uint8_t* k_cache,
                                        int page_size, int Hq, int Hkv, int Dqk, int Dv, float softmax_scale,
                                        int split_keys, void* workspace, long long workspace_bytes, int lean,
                                        void* stream);
+
+/*
+ * zyfa_attn_decode_fp8_paged_noalloc -- zyfa_attn_decode_fp8_paged for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, and harnesses that forbid
+ * device allocations. It takes no workspace: the splits' partial results go to a device
+ * array of 8 MiB (ZYFA_NOALLOC_SCRATCH_BYTES) that the library holds on every GPU it runs
+ * on, from the first such call on that GPU until the process ends. The call allocates and
+ * frees nothing (no hipMalloc, hipFree or allocating library routine); the caller still
+ * passes the inputs and outputs.
+ *
+ * Arguments, layouts, results and errors as zyfa_attn_decode_fp8_paged without workspace
+ * and workspace_bytes. A call whose partial results would need more than
+ * ZYFA_NOALLOC_SCRATCH_BYTES (zyfa_attn_decode_workspace_bytes) fails with
+ * ZYFA_ERR_UNSUPPORTED before any device work; larger split_keys need less. Every call on
+ * one GPU shares that GPU's array, and nothing in it needs to start at zero (each split
+ * writes all of its partial results before the merge reads them): calls that overlap on
+ * one GPU (on different streams, or from different threads without ordering) race and give
+ * undefined output; calls ordered on one stream are safe.
+ */
+#define ZYFA_NOALLOC_SCRATCH_BYTES (8LL << 20)
+
+zyfa_status zyfa_attn_decode_fp8_paged_noalloc(const uint8_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                               const float* q_scale, const float* k_cache_scale,
+                                               const float* v_cache_scale, int scale_block, uint16_t* o, float* lse,
+                                               const int* kv_lens, const int* block_table, int B, int max_kv_len,
+                                               int max_pages, int num_pages, int page_size, int Hq, int Hkv, int Dqk,
+                                               int Dv, float softmax_scale, int split_keys, int lean, void* stream);
 
 zyfa_status zyfa_attn_decode_bf16_paged(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
                                         uint16_t* o, float* lse, const int* kv_lens, const int* block_table, int B,

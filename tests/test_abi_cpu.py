@@ -40,14 +40,14 @@ def test_exports_every_declared_symbol(lib):
                           "zyfa_attn_fwd_fp8_range", "zyfa_attn_fwd_bf16_range", "zyfa_attn_merge",
                           "zyfa_attn_fwd_fp8_varlen", "zyfa_attn_fwd_bf16_varlen", "zyfa_attn_fwd_fp8_paged",
                           "zyfa_attn_fwd_bf16_paged", "zyfa_attn_decode_workspace_bytes", "zyfa_attn_decode_fp8_paged",
-                          "zyfa_attn_decode_bf16_paged"}
+                          "zyfa_attn_decode_bf16_paged", "zyfa_attn_decode_fp8_paged_noalloc"}
     raw = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.zyfa_abi_version() == 5
+    assert lib.zyfa_abi_version() == 6
     assert lib.zyfa_status_string(0) == b"ZYFA_OK"
     assert lib.zyfa_status_string(1) == b"ZYFA_ERR_INVALID_ARGUMENT"
     assert lib.zyfa_status_string(2) == b"ZYFA_ERR_UNSUPPORTED"
@@ -229,6 +229,29 @@ def test_decode_argument_checks(lib, kw, expect):
     assert bf16_decode(lib, **kw) == expect
     assert lib.zyfa_last_error() != b""
     assert fp8_decode(lib, **kw) == expect
+
+
+def fp8_decode_noalloc(lib, q=P, k=P2, v=P3, qs=P4, ks=P5, vs=P6, blk=128, o=P7, lse=None, kvl=0x90000, bt=0xA0000, B=4,
+                       maxkv=1000, maxp=8, nump=30, page=128, Hq=8, Hkv=2, Dqk=128, Dv=128, scale=0.088, split=256,
+                       lean=0):
+    return lib.zyfa_attn_decode_fp8_paged_noalloc(q, k, v, qs, ks, vs, blk, o, lse, kvl, bt, B, maxkv, maxp, nump, page,
+                                                  Hq, Hkv, Dqk, Dv, scale, split, lean, None)
+
+
+def test_decode_noalloc_checks():
+    # the allocation-free decode rejects calls whose partial results exceed its 8 MiB scratch
+    # array, before any device work, and otherwise checks its arguments as the decode with a
+    # workspace does (these calls fail on the host: no GPU is touched)
+    lib = _lib.load()
+    big = dict(B=64, Hq=64, Hkv=8, maxkv=1 << 20, maxp=8192, split=64)
+    need = lib.zyfa_attn_decode_workspace_bytes(64, 64, 128, 1 << 20, 64)
+    assert need > 8 << 20
+    assert fp8_decode_noalloc(lib, **big) == UNSUPPORTED
+    assert b"8388608" in lib.zyfa_last_error()
+    for kw in (dict(q=None), dict(o=MIS), dict(kvl=None), dict(B=0), dict(split=100), dict(lean=2), dict(blk=32),
+               dict(scale=-1.0), dict(Dqk=64, Dv=64)):
+        assert fp8_decode_noalloc(lib, **kw) in (INVALID, UNSUPPORTED), kw
+        assert fp8_decode_noalloc(lib, **kw) == fp8_decode(lib, **kw), kw
 
 
 @pytest.mark.parametrize("kw", [dict(qs=None), dict(vs=MIS), dict(blk=32), dict(lean=2), dict(page=64, blk=128)])
