@@ -120,7 +120,8 @@ zyfa_status zyfa_quantize_fp8(const void* x, int x_is_bf16, uint8_t* codes, floa
  *                units of 1 / rv of the latest key tile and multiplied by the ratio
  *                when rv changes, so the probabilities and their rounding do not
  *                depend on V. A zero, negative or non-finite scale gives undefined
- *                output.
+ *                output, and so do dequantized V values of magnitude 2^73 or more (the
+ *                unnormalised output, accumulated in float32, could overflow).
  *   scale_block  tokens per scale: 64 or 128.
  *   o            out: [B, Hq, S, Dv] bfloat16 (round-to-nearest-even).
  *   lse          out, may be NULL: [B, Hq, S] float32, natural-log log-sum-exp of

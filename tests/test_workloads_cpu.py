@@ -22,7 +22,8 @@ def test_shapes_and_determinism():
 def test_rising_scores_outgrow_a_lazy_reference_many_times():
     # base-2 logits of the last row, tile maxima over 64 keys: starting from the ceiling
     # of the first tile's maximum, count how often a tile's maximum exceeds the current
-    # reference by more than 8 (each such tile moves the reference to its ceiling)
+    # reference by more than the kernels' lazy threshold of 24 binades (each such tile
+    # moves the reference to its ceiling)
     for dqk in (128, 192):
         w = custom(1, 2, 1, 2048, dqk, 128, dist="rising", wid=950)
         q, k, _ = generate(w, seed=0)
@@ -33,6 +34,6 @@ def test_rising_scores_outgrow_a_lazy_reference_many_times():
             assert 4.0 < growth < 6.0  # about 5 binades per tile
             ref, moves = math.ceil(tile_max[0]), 0
             for m in tile_max[1:]:
-                if m > ref + 8:
+                if m > ref + 24:
                     ref, moves = math.ceil(m), moves + 1
-            assert moves >= 10
+            assert moves >= 5
