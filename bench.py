@@ -27,6 +27,13 @@ shape on Gaussian, activation-like (with and without rotation) and rising-score 
 The activation-like workload's record in ``other_workloads`` carries, besides times, its
 error figures with and without rotation (kernel against the oracle on the codes it read,
 input quantization against unquantized inputs), computed in the CPU leg.
+
+``--operand-zeros`` runs only the headline FP8 exact, FP8 lean and BF16 kernels with Q, K,
+V or all three zeroed, each under the sustained telemetry, to show how the operands' bits
+set the clock the board holds. ``--isa-costs`` runs only the instruction-cost probe built next to the library
+(fp8_causal_prefill_amd/isa_cost: cycles per matrix instruction for e4m3 and e2m1
+operands, SIMD cycles per vector instruction the softmax uses, and how matrix and
+vector instructions of one wave overlap) and prints its figures as one JSON line.
 """
 
 import argparse
@@ -34,6 +41,7 @@ import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -283,6 +291,42 @@ def structured_sustained(tel, window_s, stream, torch, zy):
         del qc, kc, vc
     del o
     torch.cuda.empty_cache()
+    return rec
+
+
+def operand_zeros(window_s, stream, torch, zy):
+    """The headline kernels on the headline shape (B=1, Hq=32, Hkv=8, S=32768, D=128) with
+    one operand tensor, or all three, set to zero and the instruction stream unchanged
+    (ZYFA, "Dependence of the Shader Clock on Operand Values"): each kernel runs back to back
+    under the same telemetry as ``sustained``, and its time, clock, power and energy per call
+    show how much of the power budget the matrix cores' operand bits take. Zero FP8 codes
+    keep their scales; zero BF16 inputs are bfloat16 zeros."""
+    from workloads import WORKLOADS, generate
+    w = WORKLOADS["gqa32k"]
+    dev = torch.device("cuda:0")
+    tel = Telemetry(torch)
+    if tel.smi is None:
+        return {"error": tel.error}
+    q, k, v = generate(w, seed=0)
+    blk, tau = w.scale_block, w.softmax_scale
+    f8 = [zy.quantize_fp8(torch.from_numpy(x).to(dev), blk) for x in (q, k, v)]
+    b16 = [torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (q, k, v)]
+    del q, k, v
+    o = torch.empty((w.B, w.Hq, w.S, w.Dv), dtype=torch.bfloat16, device=dev)
+    rec = {"shape": f"B={w.B} Hq={w.Hq} Hkv={w.Hkv} S={w.S} D={w.Dqk}", "settle_s": 1.5, "window_s": window_s}
+    for zero in ("none", "q", "k", "v", "qkv"):
+        codes = [torch.zeros_like(c) if n in zero else c for n, (c, _) in zip("qkv", f8)]
+        scales = [s for _, s in f8]
+        bf = [torch.zeros_like(x) if n in zero else x for n, x in zip("qkv", b16)]
+        kernels = [("fp8", lambda: zy.attn_fwd_fp8(*codes, *scales, blk, tau, o=o), PEAK_FP8),
+                   ("fp8_lean", lambda: zy.attn_fwd_fp8(*codes, *scales, blk, tau, o=o, lean=True), PEAK_FP8),
+                   ("bf16", lambda: zy.attn_fwd_bf16(*bf, tau, o=o), PEAK_BF16)]
+        for name, fn, peak in kernels:
+            r = sustained(tel, fn, w.flops, peak, 1.5, window_s, stream, torch)
+            rec[f"{name}_zero_{zero}"] = r
+            print(f"[bench] zero {zero} {name}: {r['ms']:.3f} ms, clock {r['gfxclk_mhz_median']} MHz, power "
+                  f"{r.get('socket_power_w')} W, {r.get('energy_per_call_j')} J/call", file=sys.stderr, flush=True)
+        del codes, bf
     return rec
 
 
@@ -603,7 +647,30 @@ def main():
                          "with clock and power telemetry (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
+    ap.add_argument("--operand-zeros", action="store_true",
+                    help="only run the headline kernels with Q, K, V or all three zeroed, under the sustained "
+                         "telemetry, and print that record as one JSON line")
+    ap.add_argument("--isa-costs", action="store_true",
+                    help="only run the instruction-cost probe (matrix and vector instruction cycles, "
+                         "matrix/vector overlap in one wave) and print its JSON line")
     args = ap.parse_args()
+
+    if args.isa_costs:
+        from fp8_causal_prefill_amd.build import PROBE
+        if not os.path.exists(PROBE):
+            sys.exit(f"{PROBE} is not built: run python -m fp8_causal_prefill_amd.build first")
+        r = subprocess.run([PROBE], capture_output=True, text=True, timeout=120)
+        if r.returncode != 0:
+            sys.exit(f"isa_cost exited with {r.returncode}: {r.stderr.strip()}")
+        print(json.dumps({"isa_costs": json.loads(r.stdout), "device": "cuda:0"}))
+        return
+
+    if args.operand_zeros:
+        import torch
+        import fp8_causal_prefill_amd as zy
+        stream = torch.cuda.current_stream()
+        print(json.dumps({"operand_zeros": operand_zeros(max(args.sustain, 1.0), stream, torch, zy)}))
+        return
 
     if args.copy_calibration:
         import torch

@@ -39,8 +39,8 @@ from ._lib import ZyfaError, load
 
 __all__ = ["quantize_fp8", "attn_fwd_fp8", "attn_fwd_bf16", "attn_fwd_fp8_range", "attn_fwd_bf16_range", "attn_merge",
            "attn_fwd_fp8_varlen", "attn_fwd_bf16_varlen", "attn_fwd_fp8_paged", "attn_fwd_bf16_paged",
-           "attn_decode_fp8_paged", "attn_decode_bf16_paged", "decode_split_keys", "ZyfaError",
-           "load", "abi_version"]
+           "attn_decode_fp8_paged", "attn_decode_fp8_paged_noalloc", "attn_decode_bf16_paged", "decode_split_keys", "ZyfaError",
+           "NOALLOC_SCRATCH_BYTES", "load", "abi_version"]
 
 
 def abi_version() -> int:

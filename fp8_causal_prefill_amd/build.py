@@ -4,6 +4,8 @@
 
 Every source is compiled by hipcc for gfx950 only, with packed FP32 instructions
 disabled, and linked into fp8_causal_prefill_amd/libzyfa.so next to this file.
+The instruction-cost probe (csrc/probes/isa_cost.hip, a stand-alone program that
+`bench.py --isa-costs` runs) is built next to it as fp8_causal_prefill_amd/isa_cost.
 """
 
 import os
@@ -17,6 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libzyfa.so")
 SOURCES = ["capi.cpp", "attn_fwd.hip", "quantize.hip", "merge.hip", "scratch.hip"]
+PROBE_SRC = os.path.join(CSRC, "probes", "isa_cost.hip")
+PROBE = os.path.join(HERE, "isa_cost")
 ARCH = "gfx950"
 
 
@@ -65,9 +69,20 @@ def build(extra_flags=(), verbose=False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
     os.replace(tmp, LIB)
+    build_probe(extra_flags)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE}")
     return LIB
+
+
+def build_probe(extra_flags=()) -> str:
+    tmp = PROBE + ".tmp"
+    cmd = [hipcc()] + common_flags() + list(extra_flags) + ["-x", "hip", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    os.replace(tmp, PROBE)
+    return PROBE
 
 
 if __name__ == "__main__":
