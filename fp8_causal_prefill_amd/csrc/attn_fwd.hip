@@ -173,6 +173,9 @@ struct AttnParams {
   // O and LSE go to rows qt * part_rows + (row of Q)
   int split_keys;
   size_t part_rows;
+  // debug (environment variable ZYFA_LDS_POISON): LDS starts as all-ones bytes, a NaN in
+  // both e4m3 and bf16, so that a read of any byte no tile copy wrote reaches the output
+  int poison_lds;
 };
 
 template <bool FP8>
@@ -558,6 +561,10 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
   for (int d = 0; d < 4; ++d) oacc[d] = v16f{0};
 
   // ---- prologue: K0, V0, K1 resident; scores and maxima of tile 0 ----
+  if (p.poison_lds) {
+    for (int i = tid; i < C::LDS_BYTES / 16; i += C::THREADS) *(v4i*)(smem + 16 * i) = v4i{-1, -1, -1, -1};
+    __syncthreads();
+  }
   fill_k(0, 0, pg0);
   fill_v(0, 0, pg0);
   if (n > 1) fill_k(1, 1, pg1);
@@ -1220,6 +1227,7 @@ static hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   p.page_shift = a.page_size == 64 ? 6 : a.page_size == 128 ? 7 : 8;
   p.split_keys = a.split_keys;
   p.part_rows = (size_t)a.part_rows;
+  p.poison_lds = lds_poison_requested() ? 1 : 0;
   p.n_qtiles = a.split_keys > 0 ? a.n_splits
                                 : ((a.cu_seqlens != nullptr ? a.max_seqlen : a.Sq) + C::BM - 1) / C::BM;
   p.scale_log2 = a.softmax_scale * kLog2e;

@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include "../../include/zyfa.h"
 #include "launch.h"
@@ -13,11 +14,19 @@ namespace {
 
 thread_local char g_last_error[512] = "";
 
+// a nonempty environment variable other than "0"
+bool env_flag(const char* name) {
+  const char* v = getenv(name);
+  return v != nullptr && v[0] != '\0' && !(v[0] == '0' && v[1] == '\0');
+}
+
 zyfa_status fail(zyfa_status st, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
   vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
   va_end(ap);
+  // ZYFA_DEBUG: every failed call also reports its message on stderr
+  if (env_flag("ZYFA_DEBUG")) fprintf(stderr, "zyfa: %s: %s\n", zyfa_status_string(st), g_last_error);
   return st;
 }
 
@@ -67,6 +76,8 @@ zyfa_status check_attn_common(const void* q, const void* k, const void* v, const
 }
 
 }  // namespace
+
+bool zyfa::lds_poison_requested() { return env_flag("ZYFA_LDS_POISON"); }
 
 extern "C" {
 

@@ -42,6 +42,10 @@ struct AttnArgs {
 // keys per tile of the attention kernels: a key window must start on a tile boundary
 constexpr int kKeyTile = 64;
 
+// Debug switch, read at every launch: a nonempty ZYFA_LDS_POISON other than "0" fills the
+// attention kernels' LDS with NaN bytes before their first tile copy.
+bool lds_poison_requested();
+
 // lean: probabilities as linear e4m3 codes instead of rounded exponentials
 hipError_t launch_attn_fwd_fp8(const AttnArgs& a, bool lean, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream);

@@ -45,6 +45,12 @@
  *              codes (0x7F, 0xFF) give undefined output.
  *   Threads    The library keeps no state between calls; calls are thread-safe.
  *              zyfa_last_error() reads a thread-local message.
+ *   Debugging  Two environment variables, read at every call: ZYFA_DEBUG (any value
+ *              but "" and "0") also prints each failed call's status and message on
+ *              stderr; ZYFA_LDS_POISON fills the attention kernels' LDS with all-ones
+ *              bytes (NaN in e4m3 and bfloat16) before their first tile copy, so that a
+ *              read of a byte no copy wrote would show in the output (results are
+ *              otherwise unchanged; the fill costs a few microseconds per launch).
  */
 #ifndef ZYFA_H
 #define ZYFA_H

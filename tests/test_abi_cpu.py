@@ -294,3 +294,40 @@ def test_binding_raises_without_device_tensors():
     with pytest.raises(ValueError):
         z.attn_fwd_bf16(torch.zeros(1, 1, 128, 128, dtype=torch.bfloat16), torch.zeros(1, 1, 128, 128, dtype=torch.bfloat16),
                         torch.zeros(1, 1, 128, 128, dtype=torch.bfloat16))
+
+
+def test_debug_env_reports_failures_on_stderr():
+    # ZYFA_DEBUG=1: a rejected call also prints its status and message on stderr; without
+    # it the library prints nothing (a child process, so that the variable is seen from the
+    # start and stderr can be read)
+    import subprocess
+    import sys
+    code = ("from fp8_causal_prefill_amd import _lib\n"
+            "lib = _lib.load()\n"
+            "st = lib.zyfa_attn_fwd_bf16(None, None, None, None, None, 1, 4, 2, 256, 128, 128, 0.088, None)\n"
+            "assert st == 1, st\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, PYTHONPATH=root)
+    env.pop("ZYFA_DEBUG", None)
+    quiet = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert quiet.returncode == 0, quiet.stderr
+    assert "zyfa:" not in quiet.stderr
+    env["ZYFA_DEBUG"] = "1"
+    loud = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert loud.returncode == 0, loud.stderr
+    assert "zyfa: ZYFA_ERR_INVALID_ARGUMENT: q, k, v and o must be non-null" in loud.stderr
+
+
+def test_lds_poison_switch_reads_the_environment(monkeypatch):
+    # the launchers' debug switch (ZYFA_LDS_POISON) follows the process environment at every
+    # launch: unset or "0" is off, anything else on (the GPU side is tests/test_gpu_lds_poison.py)
+    fn = ctypes.CDLL(_lib.LIB_PATH)._ZN4zyfa20lds_poison_requestedEv
+    fn.restype = ctypes.c_bool
+    monkeypatch.delenv("ZYFA_LDS_POISON", raising=False)
+    assert not fn()
+    monkeypatch.setenv("ZYFA_LDS_POISON", "1")
+    assert fn()
+    monkeypatch.setenv("ZYFA_LDS_POISON", "0")
+    assert not fn()
+    monkeypatch.setenv("ZYFA_LDS_POISON", "")
+    assert not fn()
