@@ -1,12 +1,14 @@
-"""The C ABI's host code under AddressSanitizer.
+"""The C ABI's host code under AddressSanitizer and UndefinedBehaviorSanitizer.
 
 capi.cpp (argument validation, dispatch and error reporting: all the host code the library
-runs before a launch) is built with g++ and -fsanitize=address against stub launchers,
+runs before a launch) is built with g++ and -fsanitize=address,undefined (undefined
+behaviour fatal) against stub launchers,
 and the CPU ABI tests (tests/test_abi_cpu.py: every entry point with every class of
 invalid request, and the workspace-size arithmetic; not the ones that need the Python
 package with torch or a child process of their own) run against that build in a child
-process with the sanitizer's runtime preloaded. Any out-of-bounds access, use after free
-or overflow in the host checks ends the child with a sanitizer report. No device code is
+process with the address sanitizer's runtime preloaded. Any out-of-bounds access, use
+after free, signed overflow or other undefined behaviour in the host checks (the
+workspace-size arithmetic's overflow guard among them) ends the child with a report. No device code is
 built or run: the stubs stand in for the kernels' launchers, which no invalid request
 reaches.
 """
@@ -53,13 +55,14 @@ def _asan_runtime():
     return p if os.path.isabs(p) and os.path.exists(p) else None
 
 
-def test_abi_host_checks_under_address_sanitizer(tmp_path):
+def test_abi_host_checks_under_sanitizers(tmp_path):
     rt = _asan_runtime()
     if rt is None or not os.path.exists(HIP_LIB):
         pytest.skip("needs g++ with libasan and the HIP runtime library")
     (tmp_path / "stubs.cpp").write_text(STUBS)
     lib = str(tmp_path / "libzyfa_asan.so")
-    cmd = ["g++", "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer", "-std=c++17",
+    cmd = ["g++", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-fno-omit-frame-pointer", "-std=c++17",
            "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-I", CSRC, "-fPIC", "-shared",
            os.path.join(CSRC, "capi.cpp"), str(tmp_path / "stubs.cpp"), "-L/opt/rocm/lib", "-lamdhip64", "-o", lib]
     b = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
@@ -68,6 +71,6 @@ def test_abi_host_checks_under_address_sanitizer(tmp_path):
     env = dict(os.environ, LD_PRELOAD=rt, ASAN_OPTIONS="detect_leaks=0", PYTHONPATH=ROOT)
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=600, cwd=ROOT)
     out = r.stdout + r.stderr
-    assert "AddressSanitizer" not in out, out[-4000:]
+    assert "AddressSanitizer" not in out and "runtime error:" not in out, out[-4000:]
     assert r.returncode == 0, out[-4000:]
     assert " passed" in r.stdout
