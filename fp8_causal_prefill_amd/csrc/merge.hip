@@ -23,7 +23,14 @@ namespace zyfa {
 
 constexpr int kMergeThreads = 256;
 
-template <int LANES>  // lanes per row = Dv / 8
+// Parts are taken in chunks of CHUNK: every load of a chunk (its log-sum-exps and its
+// 16-byte pieces of O) is issued before any is used, so a decode merge (few rows, many
+// parts) waits for one memory round trip per chunk instead of one per part. The launcher
+// takes the least chunk of 2, 4, 8 or 16 that holds all parts (fewer registers, more
+// waves, for the HBM-bound merges of many rows and few parts); then the maximum is final
+// before any weight is formed. Beyond 16 parts the running maximum moves chunk by chunk
+// and the sums are rescaled by exp(old - new).
+template <int LANES, int CHUNK>  // lanes per row = Dv / 8
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const uint16_t* __restrict__ o_parts,
                                                                    const float* __restrict__ lse_parts,
                                                                    int n_parts, uint16_t* __restrict__ o,
@@ -33,24 +40,43 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const uint16_
   const int sub = threadIdx.x % LANES;
   const long long stride = (long long)gridDim.x * ROWS_PER_BLOCK;
   for (long long r = (long long)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / LANES; r < rows; r += stride) {
-    // (the part loops are unrolled so that several parts' loads are in flight at once: a
-    // decode merge has few rows and many parts; the sums keep their order)
     float m = -INFINITY;
-#pragma unroll 8
-    for (int p = 0; p < n_parts; ++p) m = fmaxf(m, lse_parts[(long long)p * rows + r]);
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     float wsum = 0.0f;
-    if (m > -INFINITY) {
-#pragma unroll 8
-      for (int p = 0; p < n_parts; ++p) {
-        const float w = expf(lse_parts[(long long)p * rows + r] - m);  // exp(-inf) = 0
-        wsum += w;
-        const uint4 x = *(const uint4*)(o_parts + ((long long)p * rows + r) * DV + 8 * sub);
-        const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+    for (int p0 = 0; p0 < n_parts; p0 += CHUNK) {
+      float l[CHUNK];
+      uint4 x[CHUNK];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] = fmaf(w, __uint_as_float(xw[i] << 16), acc[2 * i]);
-          acc[2 * i + 1] = fmaf(w, __uint_as_float(xw[i] & 0xffff0000u), acc[2 * i + 1]);
+      for (int i = 0; i < CHUNK; ++i) {
+        const int p = p0 + i;
+        if (p < n_parts) {
+          l[i] = lse_parts[(long long)p * rows + r];
+          x[i] = *(const uint4*)(o_parts + ((long long)p * rows + r) * DV + 8 * sub);
+        } else {
+          l[i] = -INFINITY;
+          x[i] = uint4{0u, 0u, 0u, 0u};
+        }
+      }
+      float mc = m;
+#pragma unroll
+      for (int i = 0; i < CHUNK; ++i) mc = fmaxf(mc, l[i]);
+      if (mc == -INFINITY) continue;  // no part so far saw a key
+      if (mc > m && m > -INFINITY) {  // (only from the second chunk on)
+        const float a = expf(m - mc);
+        wsum *= a;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] *= a;
+      }
+      m = mc;
+#pragma unroll
+      for (int i = 0; i < CHUNK; ++i) {
+        const float w = expf(l[i] - m);  // exp(-inf) = 0
+        wsum += w;
+        const uint32_t xw[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[2 * j] = fmaf(w, __uint_as_float(xw[j] << 16), acc[2 * j]);
+          acc[2 * j + 1] = fmaf(w, __uint_as_float(xw[j] & 0xffff0000u), acc[2 * j + 1]);
         }
       }
     }
@@ -71,8 +97,14 @@ static hipError_t launch_merge_t(const MergeArgs& a, hipStream_t stream) {
   const long long blocks = (a.rows + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
   // a grid-stride loop covers any row count; 8192 workgroups keep all 256 CUs busy
   const unsigned grid = (unsigned)(blocks < 8192 ? blocks : 8192);
-  hipLaunchKernelGGL((attn_merge_kernel<LANES>), dim3(grid), dim3(kMergeThreads), 0, stream, a.o_parts,
-                     a.lse_parts, a.n_parts, a.o, a.lse, a.rows);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kMergeThreads), 0, stream, a.o_parts, a.lse_parts, a.n_parts, a.o,
+                       a.lse, a.rows);
+  };
+  if (a.n_parts <= 2) go(attn_merge_kernel<LANES, 2>);
+  else if (a.n_parts <= 4) go(attn_merge_kernel<LANES, 4>);
+  else if (a.n_parts <= 8) go(attn_merge_kernel<LANES, 8>);
+  else go(attn_merge_kernel<LANES, 16>);
   return hipGetLastError();
 }
 
