@@ -28,6 +28,7 @@ SHAPES = [
     (1, 1, 1, 128, 128, 128, 64),     # the tiny workload's shape
     (1, 4, 4, 1024, 128, 128, 128),   # several query tiles, MHA
     (2, 8, 2, 333, 128, 128, 64),     # GQA, ragged S, B = 2
+    (2, 4, 2, 700, 128, 128, 128),    # B * Hq = 8 with Hq not a multiple of 8 (the other XCD head map)
     (1, 4, 1, 64, 128, 128, 128),     # S below one query tile
     (1, 2, 2, 1, 128, 128, 64),       # a single token
     (1, 4, 4, 300, 192, 128, 128),    # MLA head shape, ragged
