@@ -66,7 +66,7 @@ extern "C" {
 typedef enum zyfa_status {
   ZYFA_OK = 0,
   ZYFA_ERR_INVALID_ARGUMENT = 1, /* null / misaligned pointer, bad size, bad scale */
-  ZYFA_ERR_UNSUPPORTED = 2,      /* a valid request this build has no kernel for */
+  ZYFA_ERR_UNSUPPORTED = 2,      /* a valid request the library has no kernel for */
   ZYFA_ERR_LAUNCH = 3            /* the HIP runtime rejected the kernel launch */
 } zyfa_status;
 
