@@ -34,6 +34,10 @@ set the clock the board holds. ``--isa-costs`` runs only the instruction-cost pr
 (fp8_causal_prefill_amd/isa_cost: cycles per matrix instruction for e4m3 and e2m1
 operands, SIMD cycles per vector instruction the softmax uses, and how matrix and
 vector instructions of one wave overlap) and prints its figures as one JSON line.
+``--isa-energy`` launches the same probe's kernels (fp8_causal_prefill_amd/libisa_cost.so)
+on every compute unit, one instruction class at a time, each back to back under the
+sustained telemetry, and prints the power, clock and energy per instruction of each class
+over that of waves that only sleep.
 """
 
 import argparse
@@ -296,6 +300,66 @@ def structured_sustained(tel, window_s, stream, torch, zy):
     del o
     torch.cuda.empty_cache()
     return rec
+
+
+def isa_energy(window_s, stream, torch):
+    """Energy per instruction class (ZYFA, "Dependence of the Shader Clock on Operand
+    Values": at the power limit the energy a kernel spends per call, not its cycles, sets its
+    time). Each case of the probe library runs one workgroup per compute unit, one
+    instruction class in a register-only loop, with launches of about 20 ms back to back for
+    the sustained window. Energy per instruction over idle = (power - power of the sleeping
+    case) x launch time / instructions per launch: the sleeping waves keep the chip's clocks
+    and a kernel resident, so the difference is what the instructions add."""
+    import ctypes
+    from fp8_causal_prefill_amd.build import PROBE_LIB
+    if not os.path.exists(PROBE_LIB):
+        sys.exit(f"{PROBE_LIB} is not built: run python -m fp8_causal_prefill_amd.build first")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.isa_energy_case_count.restype = ctypes.c_int
+    lib.isa_energy_case_name.restype = ctypes.c_char_p
+    lib.isa_energy_case_name.argtypes = [ctypes.c_int]
+    lib.isa_energy_case_instructions.restype = ctypes.c_double
+    lib.isa_energy_case_instructions.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.isa_energy_launch.restype = ctypes.c_int
+    lib.isa_energy_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    tel = Telemetry(torch)
+    if tel.smi is None:
+        return {"error": tel.error}
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def launch(i, iters):
+        rc = lib.isa_energy_launch(i, iters, sp)
+        if rc != 0:
+            raise RuntimeError(f"isa_energy_launch({i}, {iters}) returned HIP error {rc}")
+
+    out, idle_w = {}, None
+    for i in range(lib.isa_energy_case_count()):
+        name = lib.isa_energy_case_name(i).decode()
+        iters, ms = 64, 0.0
+        while iters < (1 << 26):  # grow until one launch takes a few ms, then aim at 20 ms
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch(i, iters)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            if ms >= 4.0:
+                break
+            iters *= 4
+        iters = max(2, min(1 << 28, int(iters * 20.0 / max(ms, 1e-3))))
+        n = lib.isa_energy_case_instructions(i, iters)
+        rec = sustained(tel, lambda: launch(i, iters), n, 1.0, 1.0, window_s, stream, torch)
+        r = {"iters": iters, "ms_per_launch": rec["ms"], "instructions_per_launch": n,
+             "gfxclk_mhz": rec.get("gfxclk_mhz_median"), "socket_power_w": rec.get("socket_power_w"),
+             "power_limited_fraction": rec.get("power_limited_fraction"),
+             "energy_per_launch_j": rec.get("energy_per_call_j")}
+        w = rec.get("socket_power_w")
+        if n == 0:
+            idle_w = w
+        elif w is not None and idle_w is not None:
+            r["pj_per_instruction_over_idle"] = (w - idle_w) * rec["ms"] * 1e-3 / n * 1e12
+        out[name] = r
+    return out
 
 
 def operand_zeros(window_s, stream, torch, zy):
@@ -659,6 +723,9 @@ def main():
     ap.add_argument("--operand-zeros", action="store_true",
                     help="only run the headline kernels with Q, K, V or all three zeroed, under the sustained "
                          "telemetry, and print that record as one JSON line")
+    ap.add_argument("--isa-energy", action="store_true",
+                    help="only run the probe library's instruction classes under the sustained telemetry "
+                         "and print power, clock and energy per instruction as one JSON line")
     ap.add_argument("--isa-costs", action="store_true",
                     help="only run the instruction-cost probe (matrix and vector instruction cycles, "
                          "matrix/vector overlap in one wave) and print its JSON line")
@@ -672,6 +739,12 @@ def main():
         if r.returncode != 0:
             sys.exit(f"isa_cost exited with {r.returncode}: {r.stderr.strip()}")
         print(json.dumps({"isa_costs": json.loads(r.stdout), "device": "cuda:0"}))
+        return
+
+    if args.isa_energy:
+        import torch
+        stream = torch.cuda.current_stream()
+        print(json.dumps({"isa_energy": isa_energy(max(args.sustain, 1.0), stream, torch), "device": "cuda:0"}))
         return
 
     if args.operand_zeros:

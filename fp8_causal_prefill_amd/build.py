@@ -4,8 +4,10 @@
 
 Every source is compiled by hipcc for gfx950 only, with packed FP32 instructions
 disabled, and linked into fp8_causal_prefill_amd/libzyfa.so next to this file.
-The instruction-cost probe (csrc/probes/isa_cost.hip, a stand-alone program that
-`bench.py --isa-costs` runs) is built next to it as fp8_causal_prefill_amd/isa_cost.
+The instruction-cost probe (csrc/probes/isa_cost.hip) is built next to it twice: as the
+stand-alone program fp8_causal_prefill_amd/isa_cost that `bench.py --isa-costs` runs, and
+as fp8_causal_prefill_amd/libisa_cost.so, whose kernels `bench.py --isa-energy` launches
+under the power telemetry.
 """
 
 import os
@@ -21,6 +23,7 @@ LIB = os.path.join(HERE, "libzyfa.so")
 SOURCES = ["capi.cpp", "attn_fwd.hip", "quantize.hip", "merge.hip", "scratch.hip"]
 PROBE_SRC = os.path.join(CSRC, "probes", "isa_cost.hip")
 PROBE = os.path.join(HERE, "isa_cost")
+PROBE_LIB = os.path.join(HERE, "libisa_cost.so")
 ARCH = "gfx950"
 
 
@@ -71,17 +74,18 @@ def build(extra_flags=(), verbose=False) -> str:
     os.replace(tmp, LIB)
     build_probe(extra_flags)
     if verbose:
-        print(f"built {LIB} and {PROBE}")
+        print(f"built {LIB}, {PROBE} and {PROBE_LIB}")
     return LIB
 
 
 def build_probe(extra_flags=()) -> str:
-    tmp = PROBE + ".tmp"
-    cmd = [hipcc()] + common_flags() + list(extra_flags) + ["-x", "hip", PROBE_SRC, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"probe build failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
-    os.replace(tmp, PROBE)
+    for out, mode in ((PROBE, []), (PROBE_LIB, ["-DISA_COST_LIB", "-shared"])):
+        tmp = out + ".tmp"
+        cmd = [hipcc()] + common_flags() + list(extra_flags) + mode + ["-x", "hip", PROBE_SRC, "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"probe build failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+        os.replace(tmp, out)
     return PROBE
 
 

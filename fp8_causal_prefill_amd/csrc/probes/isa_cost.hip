@@ -13,6 +13,11 @@
 //  * LDS reads: bytes per clock per CU for ds_read_b128 and the two transposing 64-bit
 //    reads the attention kernels use for V (8-bit and 16-bit elements), four waves per
 //    SIMD, each wave reading a contiguous run of addresses.
+//
+// Built a second time as a shared library (-DISA_COST_LIB, no main), the same kernels serve
+// energy measurements: isa_energy_launch() runs one case on every CU of the chip for a given
+// number of iterations on a caller's stream, so that a caller sampling the board's power can
+// attribute energy to each instruction class (see the isa_energy_* declarations below).
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -24,6 +29,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef __attribute__((address_space(3))) v4bf lds_v4bf;
 
@@ -40,12 +46,13 @@ constexpr int kBlocks = 256;
 constexpr int kMaxThreads = 1024;
 
 // ---- matrix instructions ----
-template <int FA, int FB, bool BIG>
+// (ONES_A: operand A is e2m1 1.0 in every element, as in the FP8 kernel's row-sum product)
+template <int FA, int FB, bool BIG, bool ONES_A = false>
 __global__ void mfma_rate(const int* in, long long* cyc, float* sink, int iters) {
   const int l = threadIdx.x & 63;
   v8i a, b;
   for (int i = 0; i < 8; ++i) {
-    a[i] = in[l * 8 + i];
+    a[i] = ONES_A ? 0x22222222 : in[l * 8 + i];
     b[i] = in[(l ^ 5) * 8 + i];
   }
   int s0 = 127, s1 = 127;
@@ -70,6 +77,39 @@ __global__ void mfma_rate(const int* in, long long* cyc, float* sink, int iters)
   if (l == 0) cyc[blockIdx.x * 16 + (threadIdx.x >> 6)] = t1 - t0;
   float s = 0;
   for (int r = 0; r < 4; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  for (int r = 0; r < 16; ++r) s += d0[r] + d1[r] + d2[r] + d3[r];
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// bf16 32x32x16 (four independent accumulators, one wave per SIMD). Each 16-bit half of an
+// input word gives one element: its sign and mantissa bits, and an exponent in [2^-15, 2^0]
+// from four more of its bits (magnitudes like the attention kernels' operands; zero words
+// give zero elements).
+__device__ inline __bf16 probe_bf16(unsigned v) {
+  const unsigned h = v & 0xffffu;
+  return __builtin_bit_cast(__bf16, (unsigned short)(h == 0 ? 0 : (h & 0x807fu) | ((112u + ((h >> 7) & 15u)) << 7)));
+}
+__global__ void mfma_bf16_rate(const int* in, long long* cyc, float* sink, int iters) {
+  const int l = threadIdx.x & 63;
+  v8bf a, b;
+  for (int i = 0; i < 4; ++i) {
+    const unsigned x = (unsigned)in[l * 4 + i], y = (unsigned)in[(l ^ 5) * 4 + i];
+    a[2 * i] = probe_bf16(x);
+    a[2 * i + 1] = probe_bf16(x >> 16);
+    b[2 * i] = probe_bf16(y);
+    b[2 * i + 1] = probe_bf16(y >> 16);
+  }
+  v16f d0 = {0}, d1 = {0}, d2 = {0}, d3 = {0};
+  const long long t0 = clock64();
+  for (int it = 0; it < iters; ++it) {
+    d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, d0, 0, 0, 0);
+    d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, d1, 0, 0, 0);
+    d2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, d2, 0, 0, 0);
+    d3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, d3, 0, 0, 0);
+  }
+  const long long t1 = clock64();
+  if (l == 0) cyc[blockIdx.x * 16 + (threadIdx.x >> 6)] = t1 - t0;
+  float s = 0;
   for (int r = 0; r < 16; ++r) s += d0[r] + d1[r] + d2[r] + d3[r];
   sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
@@ -181,9 +221,50 @@ __global__ void __launch_bounds__(1024) lds_rate(const int* in, long long* cyc, 
   sink[blockIdx.x * blockDim.x + threadIdx.x] = (float)(acc0 ^ acc1);
 }
 
+// ---- idle and scalar baselines for the energy cases ----
+__global__ void sleep_loop(const int* in, long long* cyc, float* sink, int iters) {
+  for (int it = 0; it < iters; ++it) __builtin_amdgcn_s_sleep(8);  // about 512 clocks
+  if ((threadIdx.x & 63) == 0) cyc[blockIdx.x * 16 + (threadIdx.x >> 6)] = iters;
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = 0.0f;
+}
+
+__global__ void salu_rate(const int* in, long long* cyc, float* sink, int iters) {
+  unsigned x = (unsigned)in[blockIdx.x & 4095], y = (unsigned)in[(blockIdx.x + 1) & 4095];
+  x = __builtin_amdgcn_readfirstlane(x);
+  y = __builtin_amdgcn_readfirstlane(y);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("s_add_u32 %0, %0, %1" : "+s"(x) : "s"(y) : "scc");
+  }
+  if ((threadIdx.x & 63) == 0) cyc[blockIdx.x * 16 + (threadIdx.x >> 6)] = x;
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = (float)x;
+}
+
 static int* g_in;
+static int* g_zero;
 static long long* g_cyc;
 static float* g_sink;
+
+// the kernels' buffers and inputs: random bytes (no e4m3 NaN codes) and zeros
+static hipError_t alloc_buffers() {
+  hipError_t e;
+  if ((e = hipMalloc(&g_in, 4096 * sizeof(int))) != hipSuccess) return e;
+  if ((e = hipMalloc(&g_zero, 4096 * sizeof(int))) != hipSuccess) return e;
+  if ((e = hipMalloc(&g_cyc, kBlocks * 16 * sizeof(long long))) != hipSuccess) return e;
+  if ((e = hipMalloc(&g_sink, kBlocks * kMaxThreads * sizeof(float))) != hipSuccess) return e;
+  static int h[4096];
+  srand(1);
+  for (int i = 0; i < 4096; ++i) {
+    // four random bytes, each an e4m3 or two e2m1 codes: signs and mantissas as random as in
+    // real operands, with e4m3's NaN codes (S.1111.111) moved to the largest finite ones
+    unsigned w = ((unsigned)rand() << 16) ^ (unsigned)rand();
+    for (int k = 0; k < 4; ++k)
+      if (((w >> (8 * k)) & 0x7fu) == 0x7fu) w ^= 1u << (8 * k);
+    h[i] = (int)w;
+  }
+  if ((e = hipMemcpy(g_in, h, sizeof(h), hipMemcpyHostToDevice)) != hipSuccess) return e;
+  return hipMemset(g_zero, 0, 4096 * sizeof(int));
+}
 
 // mean over CUs of the slowest wave's cycles
 template <class K>
@@ -205,14 +286,66 @@ static double simd_cycles(K kernel, int waves_per_simd, int iters) {
   return s / kBlocks;
 }
 
+// ---- energy cases: every case runs one workgroup per CU (256), with the waves per SIMD
+// given, for `iters` iterations; instructions are counted per wave64 instruction ----
+typedef void (*ProbeKernel)(const int*, long long*, float*, int);
+struct EnergyCase {
+  const char* name;
+  ProbeKernel kernel;
+  int waves_per_simd;
+  bool zero_input;
+  double per_iteration;  // instructions of the measured class per wave and iteration
+};
+static const EnergyCase kEnergyCases[] = {
+    {"idle (s_sleep, 2 waves per SIMD)", sleep_loop, 2, false, 0.0},
+    {"s_add_u32 (2 waves per SIMD)", salu_rate, 2, false, 16.0},
+    {"mfma 32x32x64 e4m3, random operands (1 wave per SIMD)", mfma_rate<0, 0, true>, 1, false, 4.0},
+    {"mfma 32x32x64 e4m3, zero operands (1 wave per SIMD)", mfma_rate<0, 0, true>, 1, true, 4.0},
+    {"mfma 32x32x64 e2m1 x e4m3, random operands (1 wave per SIMD)", mfma_rate<4, 0, true>, 1, false, 4.0},
+    {"mfma 32x32x64 e2m1 ones x e4m3 random (1 wave per SIMD)", mfma_rate<4, 0, true, true>, 1, false, 4.0},
+    {"mfma 32x32x16 bf16, random operands (1 wave per SIMD)", mfma_bf16_rate, 1, false, 4.0},
+    {"mfma 32x32x16 bf16, zero operands (1 wave per SIMD)", mfma_bf16_rate, 1, true, 4.0},
+    {"v_fma_f32 (2 waves per SIMD)", valu_rate<0, 8, false>, 2, false, 64.0},
+    {"v_exp_f32 (2 waves per SIMD)", valu_rate<1, 8, false>, 2, false, 64.0},
+    {"v_cvt_pk_fp8_f32 (2 waves per SIMD)", valu_rate<2, 8, false>, 2, false, 64.0},
+    {"v_max3_f32 (2 waves per SIMD)", valu_rate<4, 8, false>, 2, false, 64.0},
+    {"ds_read_b128 (4 waves per SIMD)", lds_rate<0>, 4, false, 8.0},
+    {"ds_read_b64_tr_b8 (4 waves per SIMD)", lds_rate<1>, 4, false, 8.0},
+    {"ds_read_b64_tr_b16 (4 waves per SIMD)", lds_rate<2>, 4, false, 8.0},
+};
+constexpr int kEnergyCaseCount = sizeof(kEnergyCases) / sizeof(kEnergyCases[0]);
+
+extern "C" {
+// number of energy cases, and the name of case i (null when i is out of range)
+int isa_energy_case_count() { return kEnergyCaseCount; }
+const char* isa_energy_case_name(int i) { return i >= 0 && i < kEnergyCaseCount ? kEnergyCases[i].name : nullptr; }
+// wave64 instructions of the case's class that one launch of `iters` iterations executes
+// (the LDS cases' loops take iterations in pairs and read one batch ahead: iters + 1 batches)
+double isa_energy_case_instructions(int i, int iters) {
+  if (i < 0 || i >= kEnergyCaseCount) return -1.0;
+  const EnergyCase& c = kEnergyCases[i];
+  const double waves = (double)kBlocks * 4 * c.waves_per_simd;
+  const bool lds = c.kernel == lds_rate<0> || c.kernel == lds_rate<1> || c.kernel == lds_rate<2>;
+  const double its = lds ? (double)((iters + 1) / 2 * 2 + 1) : (double)iters;
+  return waves * its * c.per_iteration;
+}
+// launches case i once on `stream` (a hipStream_t; null for the default stream) without
+// waiting for it; buffers are allocated on the first call. Returns a hipError_t code: 0 on
+// success, hipErrorInvalidValue for an unknown case or iters outside [2, 2^30].
+int isa_energy_launch(int i, int iters, void* stream) {
+  if (i < 0 || i >= kEnergyCaseCount || iters < 2 || iters > (1 << 30)) return (int)hipErrorInvalidValue;
+  static hipError_t ready = alloc_buffers();
+  if (ready != hipSuccess) return (int)ready;
+  const EnergyCase& c = kEnergyCases[i];
+  hipLaunchKernelGGL(c.kernel, dim3(kBlocks), dim3(256 * c.waves_per_simd), 0, (hipStream_t)stream,
+                     c.zero_input ? g_zero : g_in, g_cyc, g_sink, iters);
+  return (int)hipGetLastError();
+}
+}
+
+#ifndef ISA_COST_LIB
 int main() {
-  CK(hipMalloc(&g_in, 4096 * sizeof(int)));
-  CK(hipMalloc(&g_cyc, kBlocks * 16 * sizeof(long long)));
-  CK(hipMalloc(&g_sink, kBlocks * kMaxThreads * sizeof(float)));
-  static int h[4096];
-  srand(1);
-  for (int i = 0; i < 4096; ++i) h[i] = rand() & 0x7e7e7e7e;  // e4m3 / e2m1 bytes, no NaN codes
-  CK(hipMemcpy(g_in, h, sizeof(h), hipMemcpyHostToDevice));
+  CK(alloc_buffers());
 
   printf("{\"matrix_cycles_per_instruction\": {");
   const int mi = 256;
@@ -260,3 +393,4 @@ int main() {
   printf("\"ds_read_b64_tr_b16\": %.0f}}\n", lr(lds_rate<2>, 8));
   return 0;
 }
+#endif
