@@ -3,6 +3,8 @@
 // no device work and touches no device state.
 #include <math.h>
 #include <stdarg.h>
+
+#include <initializer_list>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -37,6 +39,18 @@ zyfa_status ok() {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Whether the product of positive factors exceeds limit (>= 0), decided without forming
+// any product larger than limit: the running product p times the next factor f exceeds
+// limit exactly when p > floor(limit / f).
+bool product_exceeds(long long limit, std::initializer_list<long long> factors) {
+  long long p = 1;
+  for (const long long f : factors) {
+    if (p > limit / f) return true;
+    p *= f;
+  }
+  return false;
+}
+
 // Largest element count any tensor may have (keeps every 64-bit offset far from overflow
 // and every per-head row count within int range).
 constexpr long long kMaxElems = 1LL << 40;
@@ -64,12 +78,12 @@ zyfa_status check_attn_common(const void* q, const void* k, const void* v, const
   if (k_begin % zyfa::kKeyTile != 0)
     return fail(ZYFA_ERR_INVALID_ARGUMENT, "k_begin (%d) must be a multiple of %d", k_begin, zyfa::kKeyTile);
   const long long dmax = Dqk > Dv ? Dqk : Dv;
-  if ((long long)B * Hq * Sq * dmax > kMaxElems || (long long)B * Hkv * Skv * dmax > kMaxElems)
+  if (product_exceeds(kMaxElems, {B, Hq, Sq, dmax}) || product_exceeds(kMaxElems, {B, Hkv, Skv, dmax}))
     return fail(ZYFA_ERR_INVALID_ARGUMENT, "tensor too large");
   if (!((Dqk == 128 && Dv == 128) || (Dqk == 192 && Dv == 128)))
     return fail(ZYFA_ERR_UNSUPPORTED, "(Dqk, Dv) = (%d, %d) is not supported; use (128, 128) or (192, 128)", Dqk, Dv);
   const long long n_qtiles = (Sq + 127) / 128;
-  if (n_qtiles * B * Hq > 0x7FFFFFFFLL) return fail(ZYFA_ERR_UNSUPPORTED, "grid too large");
+  if (product_exceeds(0x7FFFFFFFLL, {n_qtiles, B, Hq})) return fail(ZYFA_ERR_UNSUPPORTED, "grid too large");
   if ((o == q || o == k || o == v) || (lse && (lse == q || lse == k || lse == v || lse == o)))
     return fail(ZYFA_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
   return ZYFA_OK;
@@ -106,11 +120,11 @@ zyfa_status zyfa_quantize_fp8(const void* x, int x_is_bf16, uint8_t* codes, floa
     return fail(ZYFA_ERR_INVALID_ARGUMENT, "B, H, S and D must be positive (got %d, %d, %d, %d)", B, H, S, D);
   if (scale_block != 64 && scale_block != 128)
     return fail(ZYFA_ERR_INVALID_ARGUMENT, "scale_block must be 64 or 128 (got %d)", scale_block);
-  if ((long long)B * H * S * D > kMaxElems) return fail(ZYFA_ERR_INVALID_ARGUMENT, "tensor too large");
+  if (product_exceeds(kMaxElems, {B, H, S, D})) return fail(ZYFA_ERR_INVALID_ARGUMENT, "tensor too large");
   if (D != 128 && D != 192) return fail(ZYFA_ERR_UNSUPPORTED, "D = %d is not supported; use 128 or 192", D);
 
   const long long nb = (S + scale_block - 1) / scale_block;
-  if (nb * B * H > 0x7FFFFFFFLL) return fail(ZYFA_ERR_UNSUPPORTED, "grid too large");
+  if (product_exceeds(0x7FFFFFFFLL, {nb, B, H})) return fail(ZYFA_ERR_UNSUPPORTED, "grid too large");
   if ((const void*)codes == x || (const void*)scales == x || (const void*)scales == (const void*)codes)
     return fail(ZYFA_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
 
@@ -195,7 +209,7 @@ static zyfa_status check_varlen(const int* cu_seqlens, int n_seqs, int max_seqle
     return fail(ZYFA_ERR_INVALID_ARGUMENT, "n_seqs and max_seqlen must be positive (got %d, %d)", n_seqs, max_seqlen);
   if (max_seqlen > T) return fail(ZYFA_ERR_INVALID_ARGUMENT, "max_seqlen (%d) exceeds T (%d)", max_seqlen, T);
   const long long n_qtiles = (max_seqlen + 127) / 128;
-  if (n_qtiles * n_seqs * Hq > 0x7FFFFFFFLL) return fail(ZYFA_ERR_UNSUPPORTED, "grid too large");
+  if (product_exceeds(0x7FFFFFFFLL, {n_qtiles, n_seqs, Hq})) return fail(ZYFA_ERR_UNSUPPORTED, "grid too large");
   return ZYFA_OK;
 }
 
@@ -252,8 +266,8 @@ static zyfa_status check_paged(const void* k_cache, const void* v_cache, const i
   if ((long long)max_pages * page_size > kMaxPosition)
     return fail(ZYFA_ERR_INVALID_ARGUMENT, "max_pages * page_size must be at most 2^30");
   const long long dmax = Dqk > Dv ? Dqk : Dv;
-  if ((long long)num_pages * Hkv * page_size * dmax > kMaxElems ||
-      (long long)n_seqs * max_pages > 0x7FFFFFFFLL)
+  if (product_exceeds(kMaxElems, {num_pages, Hkv, page_size, dmax}) ||
+      product_exceeds(0x7FFFFFFFLL, {n_seqs, max_pages}))
     return fail(ZYFA_ERR_INVALID_ARGUMENT, "tensor too large");
   if (k_cache == v_cache) return fail(ZYFA_ERR_INVALID_ARGUMENT, "k_cache and v_cache must be distinct");
   return ZYFA_OK;
@@ -355,7 +369,7 @@ static zyfa_status decode_paged(const void* q, const void* k_cache, const void* 
     return fail(ZYFA_ERR_INVALID_ARGUMENT, "split_keys (%d) must be a positive multiple of %d", split_keys,
                 zyfa::kKeyTile);
   const long long parts = decode_splits(max_kv_len, split_keys);
-  if (parts * B * Hkv > 0x7FFFFFFFLL) return fail(ZYFA_ERR_UNSUPPORTED, "grid too large");
+  if (product_exceeds(0x7FFFFFFFLL, {parts, B, Hkv})) return fail(ZYFA_ERR_UNSUPPORTED, "grid too large");
   const long long need = zyfa_attn_decode_workspace_bytes(B, Hq, Dv, max_kv_len, split_keys);
   if (need < 0) return fail(ZYFA_ERR_UNSUPPORTED, "the splits' partial results would exceed 2^60 bytes");
   if (use_scratch) {
@@ -462,7 +476,7 @@ zyfa_status zyfa_attn_merge(const uint16_t* o_parts, const float* lse_parts, int
     return fail(ZYFA_ERR_INVALID_ARGUMENT, "n_parts and rows must be positive (got %d, %lld)", n_parts, rows);
   if (Dv != 64 && Dv != 128 && Dv != 256 && Dv != 512)
     return fail(ZYFA_ERR_UNSUPPORTED, "Dv = %d is not supported; use 64, 128, 256 or 512", Dv);
-  if ((long long)n_parts * rows * Dv > kMaxElems) return fail(ZYFA_ERR_INVALID_ARGUMENT, "tensor too large");
+  if (product_exceeds(kMaxElems, {n_parts, rows, Dv})) return fail(ZYFA_ERR_INVALID_ARGUMENT, "tensor too large");
   if ((const void*)o == (const void*)o_parts || (const void*)o == (const void*)lse_parts ||
       (lse && ((const void*)lse == (const void*)o_parts || (const void*)lse == (const void*)lse_parts ||
                (const void*)lse == (const void*)o)))

@@ -288,6 +288,28 @@ def test_quantize_argument_checks(lib, kw, expect):
     assert quant(lib, **kw) == expect
 
 
+BIG = (1 << 31) - 1
+
+
+def test_size_checks_do_not_overflow(lib):
+    # dimensions whose products pass 2^63: each is refused as too large, and no size check
+    # forms such a product (the host sanitizer run of this file reports signed overflow)
+    assert bf16(lib, B=BIG, Hq=BIG, Hkv=1, S=1 << 29) == INVALID
+    assert fp8(lib, B=BIG, Hq=BIG, Hkv=1, S=1 << 29) == INVALID
+    assert b"too large" in lib.zyfa_last_error()
+    assert fp8_range(lib, B=BIG, Hq=BIG, Hkv=BIG, Sq=1 << 29, Skv=BIG, q_offset=0, k_end=1 << 20) == INVALID
+    assert quant(lib, B=BIG, H=BIG, S=BIG, D=BIG) == INVALID
+    assert b"too large" in lib.zyfa_last_error()
+    assert merge(lib, n=8, rows=1 << 62) == INVALID
+    assert b"too large" in lib.zyfa_last_error()
+    # one sequence of 64 tokens, 2^24 heads (1 x 2^24 x 64 x 128 elements pass), a cache
+    # of 2^31 - 1 pages of 256 tokens: 2^70 elements
+    kw = dict(n=1, maxs=64, T=64, Hq=1 << 24, Hkv=1 << 24, maxp=1, nump=BIG, page=256)
+    assert bf16_paged(lib, **kw) == INVALID
+    assert fp8_paged(lib, **kw) == INVALID
+    assert b"too large" in lib.zyfa_last_error()
+
+
 def test_binding_raises_without_device_tensors():
     import torch
     import fp8_causal_prefill_amd as z
