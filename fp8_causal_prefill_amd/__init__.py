@@ -47,8 +47,14 @@ def abi_version() -> int:
     return load().zyfa_abi_version()
 
 
-def _stream():
-    return torch.cuda.current_stream().cuda_stream
+def _stream(*tensors):
+    """The current stream of the one device that holds all of a call's tensors (None
+    entries skipped): the library enqueues its kernels on that stream, and the
+    allocation-free decode finds that device's scratch array through it."""
+    devices = {t.device for t in tensors if t is not None}
+    if len(devices) != 1:
+        raise ValueError(f"a call's tensors must all be on one device, got {sorted(str(d) for d in devices)}")
+    return torch.cuda.current_stream(devices.pop()).cuda_stream
 
 
 def _dev(t: torch.Tensor, name: str, dtype, ndim: int):
@@ -81,9 +87,10 @@ def quantize_fp8(x: torch.Tensor, scale_block: int = 128, hadamard: bool = False
     ps = _dev(scales, "scales", torch.float32, 3)
     if tuple(codes.shape) != (B, H, S, D) or tuple(scales.shape) != (B, H, nb):
         raise ValueError("codes / scales have the wrong shape")
+    stream = _stream(x, codes, scales)
     lib = load()
     st = lib.zyfa_quantize_fp8(px, int(x.dtype == torch.bfloat16), pc, ps, B, H, S, D, scale_block,
-                               int(bool(hadamard)), _stream())
+                               int(bool(hadamard)), stream)
     _lib.check(st, "zyfa_quantize_fp8")
     return codes, scales
 
@@ -132,8 +139,9 @@ def attn_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, scale_block: int, softmax_s
         softmax_scale = 1.0 / math.sqrt(Dqk)
     o, po, lse, plse = _outputs(q, B, Hq, S, Dv, o, lse, return_lse)
     name = "zyfa_attn_fwd_fp8_lean" if lean else "zyfa_attn_fwd_fp8"
+    stream = _stream(q, k, v, q_scale, k_scale, v_scale, o, lse)
     st = getattr(load(), name)(pq, pk, pv, psq, psk, psv, scale_block, po, plse, B, Hq, Hkv, S, Dqk, Dv,
-                               float(softmax_scale), _stream())
+                               float(softmax_scale), stream)
     _lib.check(st, name)
     return o, lse
 
@@ -147,7 +155,8 @@ def attn_fwd_bf16(q, k, v, softmax_scale=None, o=None, lse=None, return_lse: boo
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(Dqk)
     o, po, lse, plse = _outputs(q, B, Hq, S, Dv, o, lse, return_lse)
-    st = load().zyfa_attn_fwd_bf16(pq, pk, pv, po, plse, B, Hq, Hkv, S, Dqk, Dv, float(softmax_scale), _stream())
+    stream = _stream(q, k, v, o, lse)
+    st = load().zyfa_attn_fwd_bf16(pq, pk, pv, po, plse, B, Hq, Hkv, S, Dqk, Dv, float(softmax_scale), stream)
     _lib.check(st, "zyfa_attn_fwd_bf16")
     return o, lse
 
@@ -185,9 +194,10 @@ def attn_fwd_fp8_range(q, k, v, q_scale, k_scale, v_scale, scale_block: int, q_o
     if k_end is None:
         k_end = Skv
     o, po, lse, plse = _outputs(q, B, Hq, Sq, Dv, o, lse, return_lse)
+    stream = _stream(q, k, v, q_scale, k_scale, v_scale, o, lse)
     st = load().zyfa_attn_fwd_fp8_range(pq, pk, pv, psq, psk, psv, scale_block, po, plse, B, Hq, Hkv, Sq, Skv,
                                         int(q_offset), int(k_begin), int(k_end), Dqk, Dv, float(softmax_scale),
-                                        int(bool(lean)), _stream())
+                                        int(bool(lean)), stream)
     _lib.check(st, "zyfa_attn_fwd_fp8_range")
     return o, lse
 
@@ -204,8 +214,9 @@ def attn_fwd_bf16_range(q, k, v, q_offset: int = 0, k_begin: int = 0, k_end=None
     if k_end is None:
         k_end = Skv
     o, po, lse, plse = _outputs(q, B, Hq, Sq, Dv, o, lse, return_lse)
+    stream = _stream(q, k, v, o, lse)
     st = load().zyfa_attn_fwd_bf16_range(pq, pk, pv, po, plse, B, Hq, Hkv, Sq, Skv, int(q_offset), int(k_begin),
-                                         int(k_end), Dqk, Dv, float(softmax_scale), _stream())
+                                         int(k_end), Dqk, Dv, float(softmax_scale), stream)
     _lib.check(st, "zyfa_attn_fwd_bf16_range")
     return o, lse
 
@@ -233,7 +244,8 @@ def attn_merge(o_parts, lse_parts, o=None, lse=None, return_lse: bool = False):
         plse = _dev(lse, "lse", torch.float32, len(out_shape) - 1)
         if tuple(lse.shape) != out_shape[:-1]:
             raise ValueError("lse has the wrong shape")
-    st = load().zyfa_attn_merge(po_p, pl_p, P, po, plse, rows, Dv, _stream())
+    stream = _stream(o_parts, lse_parts, o, lse)
+    st = load().zyfa_attn_merge(po_p, pl_p, P, po, plse, rows, Dv, stream)
     _lib.check(st, "zyfa_attn_merge")
     return o, lse
 
@@ -282,9 +294,10 @@ def attn_fwd_fp8_varlen(q, k, v, q_scale, k_scale, v_scale, scale_block: int, cu
         raise ValueError("scale tensors have the wrong shape")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(Dqk)
+    stream = _stream(q, k, v, q_scale, k_scale, v_scale, cu_seqlens, o, lse)
     st = load().zyfa_attn_fwd_fp8_varlen(pq, pk, pv, psq, psk, psv, scale_block, po, plse, pcu, n_seqs,
                                          int(max_seqlen), Hq, Hkv, T, Dqk, Dv, float(softmax_scale), int(bool(lean)),
-                                         _stream())
+                                         stream)
     _lib.check(st, "zyfa_attn_fwd_fp8_varlen")
     return o, lse
 
@@ -299,8 +312,9 @@ def attn_fwd_bf16_varlen(q, k, v, cu_seqlens, max_seqlen: int, softmax_scale=Non
                                                                         return_lse)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(Dqk)
+    stream = _stream(q, k, v, cu_seqlens, o, lse)
     st = load().zyfa_attn_fwd_bf16_varlen(pq, pk, pv, po, plse, pcu, n_seqs, int(max_seqlen), Hq, Hkv, T, Dqk, Dv,
-                                          float(softmax_scale), _stream())
+                                          float(softmax_scale), stream)
     _lib.check(st, "zyfa_attn_fwd_bf16_varlen")
     return o, lse
 
@@ -360,9 +374,11 @@ def attn_fwd_fp8_paged(q, k_cache, v_cache, q_scale, k_cache_scale, v_cache_scal
         raise ValueError("scale tensors have the wrong shape")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(Dqk)
+    stream = _stream(q, k_cache, v_cache, q_scale, k_cache_scale, v_cache_scale, cu_seqlens, kv_lens, block_table, o,
+                     lse)
     st = load().zyfa_attn_fwd_fp8_paged(pq, pk, pv, psq, psk, psv, scale_block, po, plse, pcu, pkl, pbt, n_seqs,
                                         int(max_seqlen), max_pages, num_pages, page_size, Hq, Hkv, T, Dqk, Dv,
-                                        float(softmax_scale), int(bool(lean)), _stream())
+                                        float(softmax_scale), int(bool(lean)), stream)
     _lib.check(st, "zyfa_attn_fwd_fp8_paged")
     return o, lse
 
@@ -377,8 +393,9 @@ def attn_fwd_bf16_paged(q, k_cache, v_cache, cu_seqlens, kv_lens, block_table, m
      plse) = _paged_common(q, k_cache, v_cache, cu_seqlens, kv_lens, block_table, max_seqlen, o, lse, return_lse)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(Dqk)
+    stream = _stream(q, k_cache, v_cache, cu_seqlens, kv_lens, block_table, o, lse)
     st = load().zyfa_attn_fwd_bf16_paged(pq, pk, pv, po, plse, pcu, pkl, pbt, n_seqs, int(max_seqlen), max_pages,
-                                         num_pages, page_size, Hq, Hkv, T, Dqk, Dv, float(softmax_scale), _stream())
+                                         num_pages, page_size, Hq, Hkv, T, Dqk, Dv, float(softmax_scale), stream)
     _lib.check(st, "zyfa_attn_fwd_bf16_paged")
     return o, lse
 
@@ -453,9 +470,10 @@ def attn_decode_fp8_paged(q, k_cache, v_cache, q_scale, k_cache_scale, v_cache_s
         raise ValueError("scale tensors have the wrong shape")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(Dqk)
+    stream = _stream(q, k_cache, v_cache, q_scale, k_cache_scale, v_cache_scale, kv_lens, block_table, o, lse, ws)
     st = load().zyfa_attn_decode_fp8_paged(pq, pk, pv, psq, psk, psv, scale_block, po, plse, pkl, pbt, B,
                                            int(max_kv_len), max_pages, num_pages, page_size, Hq, Hkv, Dqk, Dv,
-                                           float(softmax_scale), split_keys, pws, nbytes, int(bool(lean)), _stream())
+                                           float(softmax_scale), split_keys, pws, nbytes, int(bool(lean)), stream)
     _lib.check(st, "zyfa_attn_decode_fp8_paged")
     del ws  # (the stream orders its reuse by the caching allocator after the kernels)
     return o, lse
@@ -507,10 +525,11 @@ def attn_decode_fp8_paged_noalloc(q, k_cache, v_cache, q_scale, k_cache_scale, v
         raise ValueError("scale tensors have the wrong shape")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(Dqk)
+    stream = _stream(q, k_cache, v_cache, q_scale, k_cache_scale, v_cache_scale, kv_lens, block_table, o, lse)
     st = load().zyfa_attn_decode_fp8_paged_noalloc(pq, pk, pv, psq, psk, psv, scale_block, po, plse, pkl, pbt, B,
                                                    int(max_kv_len), block_table.shape[1], num_pages, page_size, Hq,
                                                    Hkv, Dqk, Dv, float(softmax_scale), int(split_keys),
-                                                   int(bool(lean)), _stream())
+                                                   int(bool(lean)), stream)
     _lib.check(st, "zyfa_attn_decode_fp8_paged_noalloc")
     return o, lse
 
@@ -526,9 +545,10 @@ def attn_decode_bf16_paged(q, k_cache, v_cache, kv_lens, block_table, max_kv_len
                               False)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(Dqk)
+    stream = _stream(q, k_cache, v_cache, kv_lens, block_table, o, lse, ws)
     st = load().zyfa_attn_decode_bf16_paged(pq, pk, pv, po, plse, pkl, pbt, B, int(max_kv_len), max_pages, num_pages,
                                             page_size, Hq, Hkv, Dqk, Dv, float(softmax_scale), split_keys, pws, nbytes,
-                                            _stream())
+                                            stream)
     _lib.check(st, "zyfa_attn_decode_bf16_paged")
     del ws
     return o, lse

@@ -402,7 +402,7 @@ static zyfa_status decode_paged(const void* q, const void* k_cache, const void* 
                   scale_block);
   }
   if (use_scratch && parts > 1) {
-    const hipError_t e = zyfa::scratch_of_current_device(&workspace);
+    const hipError_t e = zyfa::scratch_of_stream_device((hipStream_t)stream, &workspace);
     if (e != hipSuccess || workspace == nullptr)
       return fail(ZYFA_ERR_LAUNCH, "device scratch lookup failed: %s", hipGetErrorString(e));
   }

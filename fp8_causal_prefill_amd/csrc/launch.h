@@ -61,9 +61,10 @@ struct QuantArgs {
 hipError_t launch_quantize_fp8(const QuantArgs& a, hipStream_t stream);
 
 // Bytes of the file-scope device scratch array of scratch.hip (per GPU), and its device
-// address on the current device (looked up once per device; the error of that lookup).
+// address on the device that `stream` belongs to (the current device for the null stream;
+// looked up once per device; the error of that lookup).
 constexpr size_t kScratchBytes = size_t(8) << 20;
-hipError_t scratch_of_current_device(void** ptr);
+hipError_t scratch_of_stream_device(hipStream_t stream, void** ptr);
 
 struct MergeArgs {
   const uint16_t* o_parts;  // [n_parts, rows, Dv] bf16

@@ -38,6 +38,8 @@
  *              from a caller's workspace).
  *   Streams    `stream` is a hipStream_t passed as void* (NULL = the null stream);
  *              all work is enqueued on it and the call returns without waiting.
+ *              Every pointer must be memory of the stream's device (for the null
+ *              stream, the current device).
  *   Errors     Argument checks happen on the host before any device work; a
  *              failing call enqueues nothing. ZYFA_ERR_LAUNCH reports a failed
  *              kernel launch. Faults inside a kernel surface at the caller's next
@@ -372,7 +374,8 @@ zyfa_status zyfa_attn_decode_fp8_paged(const uint8_t* q, const uint8_t* k_cache,
  * allocate: code under HIP graph capture, tight serving loops, and harnesses that forbid
  * device allocations. It takes no workspace: the splits' partial results go to a device
  * array of 8 MiB (ZYFA_NOALLOC_SCRATCH_BYTES) that the library holds on every GPU it runs
- * on, from the first such call on that GPU until the process ends. The call allocates and
+ * on, from the first such call on that GPU until the process ends; a call uses the array
+ * of its stream's device. The call allocates and
  * frees nothing (no hipMalloc, hipFree or allocating library routine); the caller still
  * passes the inputs and outputs.
  *

@@ -310,6 +310,15 @@ def test_size_checks_do_not_overflow(lib):
     assert b"too large" in lib.zyfa_last_error()
 
 
+def test_binding_takes_the_stream_of_one_device():
+    import torch
+    import fp8_causal_prefill_amd as z
+    with pytest.raises(ValueError, match="one device"):
+        z._stream(torch.zeros(1), torch.zeros(1, device="meta"))
+    with pytest.raises(ValueError, match="one device"):
+        z._stream(None, None)
+
+
 def test_binding_raises_without_device_tensors():
     import torch
     import fp8_causal_prefill_amd as z

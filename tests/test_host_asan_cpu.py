@@ -31,7 +31,7 @@ hipError_t launch_attn_fwd_fp8(const AttnArgs&, bool, hipStream_t) { return hipE
 hipError_t launch_attn_fwd_bf16(const AttnArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_quantize_fp8(const QuantArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_attn_merge(const MergeArgs&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t scratch_of_current_device(void**) { return hipErrorNotSupported; }
+hipError_t scratch_of_stream_device(hipStream_t, void**) { return hipErrorNotSupported; }
 }  // namespace zyfa
 """
 

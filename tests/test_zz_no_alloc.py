@@ -77,6 +77,25 @@ def test_noalloc_decode_equals_workspace_decode_twice():
     assert torch.equal(o4, o4_ref) and torch.equal(lse4, l4_ref)
 
 
+def test_noalloc_decode_on_a_side_stream():
+    # a stream other than the null stream: the library finds the scratch array of the
+    # stream's device from the stream itself
+    Hq, Hkv, D, P, block = 8, 2, 128, 128, 64
+    lens = [70, 1300, 2000]
+    _case("noalloc on a side stream", lens)
+    ops = _decode_inputs(lens, P, Hq, Hkv, D, block, seed=4)
+    o_ref, lse_ref, _, _ = _both(ops, block, max(lens), 128)
+    side = torch.cuda.Stream()  # (default priority)
+    side.wait_stream(torch.cuda.current_stream())
+    qc, kc, vc, qs, ks, vs, kvl, bt = ops
+    o = torch.empty_like(o_ref)
+    lse = torch.empty_like(lse_ref)
+    with torch.cuda.stream(side):
+        zy.attn_decode_fp8_paged_noalloc(qc, kc, vc, qs, ks, vs, block, kvl, bt, max(lens), o, lse, split_keys=128)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
+
+
 def test_noalloc_decode_rejects_requests_beyond_its_scratch():
     Hq, Hkv, D, P, block = 64, 8, 128, 128, 64
     _case("noalloc too large")
