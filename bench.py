@@ -37,7 +37,10 @@ vector instructions of one wave overlap) and prints its figures as one JSON line
 ``--isa-energy`` launches the same probe's kernels (fp8_causal_prefill_amd/libisa_cost.so)
 on every compute unit, one instruction class at a time, each back to back under the
 sustained telemetry, and prints the power, clock and energy per instruction of each class
-over that of waves that only sleep.
+over that of waves that only sleep. ``--timeline`` runs the headline-shape kernels (or
+``--workload``'s) once each from the timeline build (fp8_causal_prefill_amd/libzyfa_timeline.so)
+and prints where each launch's time goes: every workgroup's prologue, key-tile loop and
+epilogue, the gaps between workgroups on a compute unit, and when each XCD goes idle.
 """
 
 import argparse
@@ -359,6 +362,117 @@ def isa_energy(window_s, stream, torch):
         elif w is not None and idle_w is not None:
             r["pj_per_instruction_over_idle"] = (w - idle_w) * rec["ms"] * 1e-3 / n * 1e12
         out[name] = r
+    return out
+
+
+def timeline_summary(rec):
+    """Summary of one launch's workgroup records (include/zyfa_timeline.h: an array
+    [workgroups, 8] of entry, loop start, loop end and exit stamps of a 100 MHz clock, the
+    HW_ID and XCC_ID registers, and the key-tile count). A compute unit is named by its XCD,
+    shader engine, shader array and CU index; workgroups that ran on one compute unit one
+    after another give the dispatcher's gaps (start of the next minus end of the previous).
+    Times in µs from the first workgroup's entry."""
+    rec = np.asarray(rec, dtype=np.int64)
+    done = rec[:, 3] > 0  # workgroups that ran the loop (the others only record their entry)
+    t0 = rec[:, 0].min()
+    t = (rec[:, :4] - t0) * 0.01  # µs
+    t[~done, 1:4] = t[~done, 0:1]
+    hw, xcc = rec[:, 4], rec[:, 5]
+    cu = ((xcc & 0xF) << 8) | (((hw >> 13) & 7) << 5) | (((hw >> 12) & 1) << 4) | ((hw >> 8) & 0xF)
+    span = float(t[:, 3].max())
+    pro, loop, epi = t[done, 1] - t[done, 0], t[done, 2] - t[done, 1], t[done, 3] - t[done, 2]
+    tiles = rec[done, 6]
+    gaps, ends, busy, xcd_of = [], [], [], []
+    for c in np.unique(cu):
+        idx = np.where(cu == c)[0]
+        order = idx[np.argsort(t[idx, 0])]
+        s0, s3 = t[order, 0], t[order, 3]
+        g = s0[1:] - s3[:-1]
+        gaps.extend(g[g >= 0].tolist())  # (overlapping workgroups on one unit give no gap)
+        ends.append(float(s3.max()))
+        busy.append(float((s3 - s0).sum()))
+        xcd_of.append(int(c) >> 8)
+    ends, busy, xcd_of = np.array(ends), np.array(busy), np.array(xcd_of)
+    gaps = np.array(gaps) if gaps else np.zeros(1)
+    unit_time = float(busy.sum() + gaps.sum())
+    return {
+        "workgroups": int(len(rec)), "compute_units": int(len(ends)), "span_us": span,
+        "prologue_us_mean": float(pro.mean()) if done.any() else None,
+        "loop_us_per_key_tile": float(loop.sum() / max(1, tiles.sum())) if done.any() else None,
+        "epilogue_us_mean": float(epi.mean()) if done.any() else None,
+        "gap_us_mean": float(gaps.mean()),
+        "transition_share": float((pro.sum() + epi.sum() + gaps.sum()) / unit_time) if unit_time > 0 else None,
+        "unit_busy_us_mean": float(busy.mean()), "unit_end_us_min": float(ends.min()), "unit_end_us_max": float(ends.max()),
+        "tail_idle_share": float(1.0 - ends.mean() / span) if span > 0 else None,
+        "xcd_end_us": [float(ends[xcd_of == x].max()) for x in sorted(set(xcd_of.tolist()))],
+        "xcd_busy_us_mean": [float(busy[xcd_of == x].mean()) for x in sorted(set(xcd_of.tolist()))],
+    }
+
+
+def timeline(workload_name, stream, torch):
+    """One launch of each prefill kernel (FP8 exact, FP8 lean, BF16) of the workload from the
+    timeline build, after ten unrecorded ones, and the summary of its workgroup records."""
+    import ctypes
+    from fp8_causal_prefill_amd.build import TIMELINE_LIB
+    from workloads import WORKLOADS, generate
+    if not os.path.exists(TIMELINE_LIB):
+        sys.exit(f"{TIMELINE_LIB} is not built: run python -m fp8_causal_prefill_amd.build first")
+    lib = ctypes.CDLL(TIMELINE_LIB)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.zyfa_quantize_fp8.argtypes = [vp, i32, vp, vp] + [i32] * 6 + [vp]
+    for fn in ("zyfa_attn_fwd_fp8", "zyfa_attn_fwd_fp8_lean"):
+        getattr(lib, fn).argtypes = [vp] * 6 + [i32, vp, vp] + [i32] * 6 + [f32, vp]
+    lib.zyfa_attn_fwd_bf16.argtypes = [vp] * 5 + [i32] * 6 + [f32, vp]
+    lib.zyfa_timeline_clear.argtypes = [vp]
+    lib.zyfa_timeline_read.argtypes = [vp, ctypes.c_longlong]
+    w = WORKLOADS[workload_name]
+    q, k, v = generate(w, seed=0)
+    dev = torch.device("cuda:0")
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def ok(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} returned {rc}")
+
+    def quant(x, H):
+        xd = torch.from_numpy(x).to(dev)
+        nb = (w.S + w.scale_block - 1) // w.scale_block
+        codes = torch.empty(xd.shape, dtype=torch.uint8, device=dev)
+        scales = torch.empty((w.B, H, nb), dtype=torch.float32, device=dev)
+        ok(lib.zyfa_quantize_fp8(xd.data_ptr(), 0, codes.data_ptr(), scales.data_ptr(), w.B, H, w.S, xd.shape[3],
+                                 w.scale_block, 0, sp), "zyfa_quantize_fp8")
+        return codes, scales, xd.bfloat16()
+
+    (qc, qs, qb), (kc, ks, kb), (vc, vs, vb) = quant(q, w.Hq), quant(k, w.Hkv), quant(v, w.Hkv)
+    o = torch.empty((w.B, w.Hq, w.S, w.Dv), dtype=torch.bfloat16, device=dev)
+    shape = (w.B, w.Hq, w.Hkv, w.S, w.Dqk, w.Dv)
+    calls = {
+        "fp8": lambda: lib.zyfa_attn_fwd_fp8(qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), qs.data_ptr(), ks.data_ptr(),
+                                             vs.data_ptr(), w.scale_block, o.data_ptr(), None, *shape,
+                                             w.softmax_scale, sp),
+        "fp8_lean": lambda: lib.zyfa_attn_fwd_fp8_lean(qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), qs.data_ptr(),
+                                                       ks.data_ptr(), vs.data_ptr(), w.scale_block, o.data_ptr(), None,
+                                                       *shape, w.softmax_scale, sp),
+        "bf16": lambda: lib.zyfa_attn_fwd_bf16(qb.data_ptr(), kb.data_ptr(), vb.data_ptr(), o.data_ptr(), None, *shape,
+                                               w.softmax_scale, sp),
+    }
+    n_wg = w.B * w.Hq * ((w.S + 255) // 256)
+    out = {"workload": workload_name, "workgroups": n_wg}
+    if n_wg > 65536:
+        out["note"] = "records cover the first 65536 workgroups"
+        n_wg = 65536
+    for name, fn in calls.items():
+        for _ in range(10):
+            ok(fn(), name)
+        ok(lib.zyfa_timeline_clear(sp), "zyfa_timeline_clear")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        ok(fn(), name)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rec = np.zeros((n_wg, 8), dtype=np.uint64)
+        ok(lib.zyfa_timeline_read(rec.ctypes.data, n_wg), "zyfa_timeline_read")
+        out[name] = dict(kernel_ms=e0.elapsed_time(e1), **timeline_summary(rec))
     return out
 
 
@@ -723,6 +837,9 @@ def main():
     ap.add_argument("--operand-zeros", action="store_true",
                     help="only run the headline kernels with Q, K, V or all three zeroed, under the sustained "
                          "telemetry, and print that record as one JSON line")
+    ap.add_argument("--timeline", action="store_true",
+                    help="only run the workload's prefill kernels once each from the timeline build and print "
+                         "the summary of their workgroup records as one JSON line")
     ap.add_argument("--isa-energy", action="store_true",
                     help="only run the probe library's instruction classes under the sustained telemetry "
                          "and print power, clock and energy per instruction as one JSON line")
@@ -739,6 +856,12 @@ def main():
         if r.returncode != 0:
             sys.exit(f"isa_cost exited with {r.returncode}: {r.stderr.strip()}")
         print(json.dumps({"isa_costs": json.loads(r.stdout), "device": "cuda:0"}))
+        return
+
+    if args.timeline:
+        import torch
+        stream = torch.cuda.current_stream()
+        print(json.dumps({"timeline": timeline(args.workload, stream, torch), "device": "cuda:0"}))
         return
 
     if args.isa_energy:

@@ -4,6 +4,9 @@
 
 Every source is compiled by hipcc for gfx950 only, with packed FP32 instructions
 disabled, and linked into fp8_causal_prefill_amd/libzyfa.so next to this file.
+The timeline build, libzyfa_timeline.so (include/zyfa_timeline.h: the same library with
+per-workgroup time stamps in the prefill kernels, read by `bench.py --timeline`), is linked
+next to it from a second compile of the attention kernels.
 The instruction-cost probe (csrc/probes/isa_cost.hip) is built next to it twice: as the
 stand-alone program fp8_causal_prefill_amd/isa_cost that `bench.py --isa-costs` runs, and
 as fp8_causal_prefill_amd/libisa_cost.so, whose kernels `bench.py --isa-energy` launches
@@ -20,6 +23,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libzyfa.so")
+TIMELINE_LIB = os.path.join(HERE, "libzyfa_timeline.so")
 SOURCES = ["capi.cpp", "attn_fwd.hip", "quantize.hip", "merge.hip", "scratch.hip"]
 PROBE_SRC = os.path.join(CSRC, "probes", "isa_cost.hip")
 PROBE = os.path.join(HERE, "isa_cost")
@@ -48,8 +52,8 @@ def common_flags():
     ]
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra, tag: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
     cmd = [hipcc()] + common_flags() + list(extra) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so: harmless
@@ -62,19 +66,26 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra_flags=(), verbose=False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra_flags), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+def _link(out: str, objs) -> None:
+    tmp = out + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + list(objs)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(extra_flags=(), verbose=False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = [(s, list(extra_flags), "") for s in SOURCES] + [("attn_fwd.hip", list(extra_flags) + ["-DZYFA_TIMELINE"],
+                                                             "_timeline")]
+    with ThreadPoolExecutor(max_workers=min(4, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    _link(LIB, objs[:len(SOURCES)])
+    _link(TIMELINE_LIB, [objs[-1] if s == "attn_fwd.hip" else o for s, o in zip(SOURCES, objs)])
     build_probe(extra_flags)
     if verbose:
-        print(f"built {LIB}, {PROBE} and {PROBE_LIB}")
+        print(f"built {LIB}, {TIMELINE_LIB}, {PROBE} and {PROBE_LIB}")
     return LIB
 
 

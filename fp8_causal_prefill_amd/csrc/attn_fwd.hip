@@ -57,8 +57,23 @@
 
 #include "device.h"
 #include "launch.h"
+#ifdef ZYFA_TIMELINE
+#include "../../include/zyfa_timeline.h"
+#endif
 
 namespace zyfa {
+
+#ifdef ZYFA_TIMELINE
+// Timeline build only (libzyfa_timeline.so): one record per workgroup of the eight-wave
+// prefill kernels, written by its first thread (fields as include/zyfa_timeline.h lists).
+// In the library proper the two hooks below expand to nothing.
+__device__ unsigned long long timeline[ZYFA_TIMELINE_WORKGROUPS * ZYFA_TIMELINE_FIELDS];
+#define ZYFA_TL_CLOCK(field) tl_put(field, __builtin_amdgcn_s_memrealtime())
+#define ZYFA_TL_PUT(field, x) tl_put(field, x)
+#else
+#define ZYFA_TL_CLOCK(field) ((void)0)
+#define ZYFA_TL_PUT(field, x) ((void)0)
+#endif
 
 // The reference moves only when a row's maximum exceeds it by more than kLazyThreshold
 // binades. The probabilities' block scaling does not depend on it (every block maximum lands
@@ -202,6 +217,18 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
   const int wave = tid >> 6;
   const int h = lane >> 5;
   const int l32 = lane & 31;
+#ifdef ZYFA_TIMELINE
+  const bool tl_on = blockIdx.x < ZYFA_TIMELINE_WORKGROUPS && tid == 0;
+  unsigned long long* const tl = timeline + (size_t)blockIdx.x * ZYFA_TIMELINE_FIELDS;
+  auto tl_put = [&](int field, unsigned long long x) {
+    if constexpr (!PAGED && WAVES == 8) {
+      if (tl_on) tl[field] = x;
+    }
+  };
+  ZYFA_TL_CLOCK(0);
+  ZYFA_TL_PUT(4, __builtin_amdgcn_s_getreg((4 << 0) | (0 << 6) | (31 << 11)));   // HW_ID
+  ZYFA_TL_PUT(5, __builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (31 << 11)));  // XCC_ID
+#endif
 
   // ---- work item: (batch, query head, query tile), heaviest tile first ----
   const int NH = p.B * p.Hq;
@@ -952,6 +979,8 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
       next_pages(pg3);
     };
 
+    ZYFA_TL_PUT(6, (unsigned long long)n);
+    ZYFA_TL_CLOCK(1);
     int t = 0;
     for (; t < n_steady; t += 2) {
       steady_step(std::false_type{}, t, sa, sb, pa, pb);
@@ -967,6 +996,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
       if (t + 1 < n) step(t + 1, sb, sa, pb, pa);
     }
     // drain: PV of the last tile (its P is pb if n - 1 is even, else pa)
+    ZYFA_TL_CLOCK(2);
     fix_units();
     pv(((n - 1) & 1) ? pa : pb, sp_prev, sv_prev, (n - 1) % C::NBUF);
 #pragma unroll
@@ -974,6 +1004,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
     pin_acc(rs_acc);
     // O = oacc * rv_o / l; the log-sum-exp from l alone
     store_out(rs_acc[0] / rv_o, LEAN ? rs_acc[0] * kLeanSumScale : rs_acc[0]);
+    ZYFA_TL_CLOCK(3);
   } else {
     // ===================== BF16: three-stage pipeline =====================
     // Iteration t: PV of tile t-1 (its P formed in iteration t-1), then the maxima of
@@ -1174,11 +1205,14 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
       idle_loop();
       return;
     }
+    ZYFA_TL_PUT(6, (unsigned long long)n);
+    ZYFA_TL_CLOCK(1);
     int t = 0;
     for (; t < n_steady_b; ++t) steady_step(std::false_type{}, t);
     for (; t + 1 < n; ++t) steady_step(std::true_type{}, t);  // the diagonal tiles
     for (; t < n; ++t) step(t);
     // drain: PV of the last tile
+    ZYFA_TL_CLOCK(2);
     fix_o();
     {
       const char* vb = vring + ((n - 1) & 1) * C::VBUF + v_off0;
@@ -1192,6 +1226,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
     for (int d = 0; d < 4; ++d) pin_acc(oacc[d]);
     const float l_sum = sum_across_halves(l_part);
     store_out(l_sum, l_sum);
+    ZYFA_TL_CLOCK(3);
   }
 }
 
@@ -1250,6 +1285,26 @@ hipError_t launch_attn_fwd_fp8(const AttnArgs& a, bool lean, hipStream_t stream)
   if (lean) return a.Dqk == 192 ? launch<true, 192, true>(a, stream) : launch<true, 128, true>(a, stream);
   return a.Dqk == 192 ? launch<true, 192>(a, stream) : launch<true, 128>(a, stream);
 }
+
+#ifdef ZYFA_TIMELINE
+}  // namespace zyfa
+
+extern "C" int zyfa_timeline_clear(void* stream) {
+  void* p = nullptr;
+  hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(zyfa::timeline));
+  if (e == hipSuccess) e = hipMemsetAsync(p, 0, sizeof(zyfa::timeline), (hipStream_t)stream);
+  return (int)e;
+}
+
+extern "C" int zyfa_timeline_read(unsigned long long* host, long long n_workgroups) {
+  if (host == nullptr || n_workgroups < 0 || n_workgroups > ZYFA_TIMELINE_WORKGROUPS) return (int)hipErrorInvalidValue;
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(zyfa::timeline),
+                                  (size_t)n_workgroups * ZYFA_TIMELINE_FIELDS * sizeof(unsigned long long), 0,
+                                  hipMemcpyDeviceToHost);
+}
+
+namespace zyfa {
+#endif
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream) {
   // (BF16 decode stays on the eight-wave workgroup: a one-wave BF16 workgroup measured

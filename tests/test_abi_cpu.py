@@ -362,3 +362,23 @@ def test_lds_poison_switch_reads_the_environment(monkeypatch):
     assert not fn()
     monkeypatch.setenv("ZYFA_LDS_POISON", "")
     assert not fn()
+
+
+def test_timeline_build_exports_the_abi_and_its_readers():
+    # libzyfa_timeline.so: the same entry points, plus the two readers of
+    # include/zyfa_timeline.h; libzyfa.so has none of the latter
+    from fp8_causal_prefill_amd.build import TIMELINE_LIB
+    tl = ctypes.CDLL(TIMELINE_LIB)
+    for n in declared_functions():
+        assert hasattr(tl, n), n
+    text = open(os.path.join(os.path.dirname(HEADER), "zyfa_timeline.h")).read()
+    readers = sorted(set(re.findall(r"\b(zyfa_timeline_[a-z]+)\s*\(", text)))
+    assert readers == ["zyfa_timeline_clear", "zyfa_timeline_read"]
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    for n in readers:
+        assert hasattr(tl, n) and not hasattr(raw, n), n
+    tl.zyfa_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong]
+    buf = (ctypes.c_ulonglong * 8)()
+    assert tl.zyfa_timeline_read(None, 1) == 1  # hipErrorInvalidValue, before any HIP call
+    assert tl.zyfa_timeline_read(buf, -1) == 1
+    assert tl.zyfa_timeline_read(buf, 65537) == 1

@@ -1,5 +1,5 @@
 """bench.py's host logic, without a GPU: the one-GPU guard, the traffic record's source
-hash check and the CPU description of the baseline."""
+hash check, the CPU description of the baseline and the summary of timeline records."""
 
 import json
 import os
@@ -38,3 +38,31 @@ def test_kernel_hash_covers_the_attention_sources():
 
 def test_cpu_model_is_named():
     assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
+
+
+def _rec(start, loop0, loop1, end, xcd, cu, tiles):
+    # stamps in the 100 MHz clock's ticks (0.01 µs); HW_ID holds the CU index in bits 8-11
+    return [start, loop0, loop1, end, cu << 8, xcd, tiles, 0]
+
+
+def test_timeline_summary_of_synthetic_records():
+    rec = [
+        _rec(0, 100, 900, 1000, xcd=0, cu=1, tiles=4),      # unit A: 0-10 µs
+        _rec(0, 100, 1800, 2000, xcd=1, cu=1, tiles=4),     # unit B: 0-20 µs
+        _rec(1200, 1300, 2100, 2200, xcd=0, cu=1, tiles=4),  # unit A again after a 2 µs gap
+    ]
+    s = bench.timeline_summary(rec)
+    assert s["workgroups"] == 3 and s["compute_units"] == 2
+    assert abs(s["span_us"] - 22.0) < 1e-9
+    assert abs(s["prologue_us_mean"] - 1.0) < 1e-9
+    assert abs(s["loop_us_per_key_tile"] - (8 + 17 + 8) / 12) < 1e-9
+    assert abs(s["epilogue_us_mean"] - 4 / 3) < 1e-9
+    assert abs(s["gap_us_mean"] - 2.0) < 1e-9
+    assert abs(s["transition_share"] - (3 + 4 + 2) / (40 + 2)) < 1e-9
+    assert s["xcd_end_us"] == [22.0, 20.0] and s["unit_end_us_min"] == 20.0
+    assert abs(s["tail_idle_share"] - (1 - 21 / 22)) < 1e-9
+    # a workgroup that saw no key records its entry only: it counts as a zero-length visit
+    s2 = bench.timeline_summary(rec + [[2100, 0, 0, 0, 1 << 8, 1, 0, 0]])
+    assert s2["workgroups"] == 4 and abs(s2["gap_us_mean"] - 1.5) < 1e-9
+    assert s2["xcd_end_us"] == [22.0, 21.0]
+    assert abs(s2["prologue_us_mean"] - 1.0) < 1e-9
