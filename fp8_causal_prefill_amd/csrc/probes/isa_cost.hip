@@ -148,6 +148,7 @@ __global__ void valu_rate(const int* in, long long* cyc, float* sink, int iters)
         else if constexpr (OP == 4) x[i] = fmaxf(fmaxf(x[i], x[(i + 1) & 15]), x[(i + 2) & 15]);
         else if constexpr (OP == 5) u[i] = __builtin_amdgcn_perm(u[i], u[(i + 1) & 15], 0x03020100u + i);
         else if constexpr (OP == 6) u[i] = __builtin_amdgcn_mov_dpp(u[i], 0xB1, 0xF, 0xF, true);
+        else if constexpr (OP == 7) x[i] = fmaf(x[i], x[i], -1.9f);  // chaotic in [-1.9, 1.97]: bits keep changing
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -219,6 +220,42 @@ __global__ void __launch_bounds__(1024) lds_rate(const int* in, long long* cyc, 
   const long long t1 = clock64();
   if (lane == 0) cyc[blockIdx.x * 16 + wave] = t1 - t0;
   sink[blockIdx.x * blockDim.x + threadIdx.x] = (float)(acc0 ^ acc1);
+}
+
+// ---- the softmax's vector work per wave-step of the exact FP8 kernel, on changing data ----
+// Per iteration and lane: 32 scores advanced by s = s^2 - 1.9 (one FMA each; the map keeps
+// s in [-1.9, 1.97] and chaotic, so operand bits change like those of real scores), their
+// exponentials, the running row maximum over them (16 three-input maxima), and their e4m3
+// codes (16 packing conversions): 96 vector instructions, the kernel's per-step mix without
+// its bookkeeping.
+__global__ void softmax_mix_rate(const int* in, long long* cyc, float* sink, int iters) {
+  const int l = threadIdx.x & 63;
+  float sc[32];
+  for (int j = 0; j < 32; ++j) sc[j] = (float)(in[(l * 32 + j) & 4095] & 0xffff) * (3.8f / 65536.0f) - 1.9f;
+  float m0 = -INFINITY, m1 = -INFINITY;
+  int pk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const long long t0 = clock64();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) sc[j] = fmaf(sc[j], sc[j], -1.9f);
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+      m0 = fmaxf(fmaxf(m0, sc[2 * j]), sc[2 * j + 1]);
+      m1 = fmaxf(fmaxf(m1, sc[2 * j + 2]), sc[2 * j + 3]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p0 = __builtin_amdgcn_exp2f(sc[4 * j]), p1 = __builtin_amdgcn_exp2f(sc[4 * j + 1]);
+      const float p2 = __builtin_amdgcn_exp2f(sc[4 * j + 2]), p3 = __builtin_amdgcn_exp2f(sc[4 * j + 3]);
+      pk[j] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pk[j], false), true);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const long long t1 = clock64();
+  if (l == 0) cyc[blockIdx.x * 16 + (threadIdx.x >> 6)] = t1 - t0;
+  int acc = 0;
+  for (int j = 0; j < 8; ++j) acc ^= pk[j];
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = m0 + m1 + (float)acc;
 }
 
 // ---- idle and scalar baselines for the energy cases ----
@@ -305,10 +342,13 @@ static const EnergyCase kEnergyCases[] = {
     {"mfma 32x32x64 e2m1 ones x e4m3 random (1 wave per SIMD)", mfma_rate<4, 0, true, true>, 1, false, 4.0},
     {"mfma 32x32x16 bf16, random operands (1 wave per SIMD)", mfma_bf16_rate, 1, false, 4.0},
     {"mfma 32x32x16 bf16, zero operands (1 wave per SIMD)", mfma_bf16_rate, 1, true, 4.0},
-    {"v_fma_f32 (2 waves per SIMD)", valu_rate<0, 8, false>, 2, false, 64.0},
+    {"v_fma_f32, converging operands (2 waves per SIMD)", valu_rate<0, 8, false>, 2, false, 64.0},
+    {"v_fma_f32 on chaotic operands, x = x * x - 1.9 (2 waves per SIMD)", valu_rate<7, 8, false>, 2, false, 64.0},
     {"v_exp_f32 (2 waves per SIMD)", valu_rate<1, 8, false>, 2, false, 64.0},
     {"v_cvt_pk_fp8_f32 (2 waves per SIMD)", valu_rate<2, 8, false>, 2, false, 64.0},
     {"v_max3_f32 (2 waves per SIMD)", valu_rate<4, 8, false>, 2, false, 64.0},
+    {"softmax mix: 32 fma, 32 exp, 16 max3, 16 cvt_pk_fp8 on chaotic scores (2 waves per SIMD)", softmax_mix_rate, 2,
+     false, 96.0},
     {"ds_read_b128 (4 waves per SIMD)", lds_rate<0>, 4, false, 8.0},
     {"ds_read_b64_tr_b8 (4 waves per SIMD)", lds_rate<1>, 4, false, 8.0},
     {"ds_read_b64_tr_b16 (4 waves per SIMD)", lds_rate<2>, 4, false, 8.0},
