@@ -650,22 +650,67 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
 
   // epilogue: O / o_div as bfloat16, and the log-sum-exp of the row sum l_sum (o_div is
   // l_sum in the units O is accumulated in: they differ when the FP8 V scale is not a power
-  // of two, and the log-sum-exp must not depend on V)
+  // of two, and the log-sum-exp must not depend on V).
+  // A lane holds half of its row's 128 values, in 8-byte pieces that alternate with the
+  // other half's lane. Stored from there, each store instruction would write 32 rows in
+  // 16-byte pieces, and a workgroup's 64 KiB of O would drain slowly, holding its compute
+  // unit. So the eight-wave prefill kernels stage each wave's rows through LDS, 64 values of
+  // each row per pass in the wave's 4 KiB (128-byte rows, 16-byte chunk c of row r at chunk
+  // c ^ (r & 7), so that the writes and the reads below hit distinct banks), and store whole
+  // 128-byte lines: 8 rows per instruction. (Decode keeps the direct stores: its rows are a
+  // few query heads, and BF16 decode has waves that leave before the epilogue.)
   auto store_out = [&](float o_div, float l_sum) {
     const int my_q = row_of_lane();
-    if (q0 >= Sq || my_q >= Sq) return;
     const float inv_l = l_sum > 0.0f ? 1.0f / o_div : 0.0f;  // a row with no key: O = 0, LSE = -inf
-    uint16_t* orow = p.o + (o_row0 + my_q) * C::DV;
+    auto piece = [&](int d, int r4) {  // values 32 d + 8 r4 + 4 h .. + 3 of this lane's row
+      uint2 w;
+      w.x = pack_bf16x2(oacc[d][4 * r4 + 0] * inv_l, oacc[d][4 * r4 + 1] * inv_l);
+      w.y = pack_bf16x2(oacc[d][4 * r4 + 2] * inv_l, oacc[d][4 * r4 + 3] * inv_l);
+      return w;
+    };
+    bool staged = C::WAVES == 8;
+    if constexpr (PAGED) staged = staged && p.split_keys == 0;
+    if (staged) {
+      static_assert(C::WAVES != 8 || C::LDS_BYTES >= 8 * 4096, "staging needs 4 KiB of LDS per wave");
+      // (uniform over the workgroup: every wave gets here) no wave still reads the K / V
+      // ring that the staging reuses
+      __syncthreads();
+      if (q0 < Sq) {
+        char* const area = smem + wave_u * 4096;
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
+        for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        uint2 w;
-        w.x = pack_bf16x2(oacc[d][4 * r4 + 0] * inv_l, oacc[d][4 * r4 + 1] * inv_l);
-        w.y = pack_bf16x2(oacc[d][4 * r4 + 2] * inv_l, oacc[d][4 * r4 + 3] * inv_l);
-        *(uint2*)(orow + 32 * d + 8 * r4 + 4 * h) = w;
+          for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const int c = 4 * dd + r4;  // 16-byte chunk of the pass's 128 bytes of the row
+              *(uint2*)(area + l32 * 128 + ((c ^ (l32 & 7)) << 4) + 8 * h) = piece(2 * pass + dd, r4);
+            }
+          // the wave's own writes, read back by other lanes of the wave
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          const int c = lane & 7;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int r = 8 * k + (lane >> 3);
+            const uint4 x = *(const uint4*)(area + r * 128 + ((c ^ (r & 7)) << 4));
+            if (q0 + r < Sq) *(uint4*)(p.o + (o_row0 + q0 + r) * C::DV + 64 * pass + 8 * c) = x;
+          }
+          // the next pass overwrites the area only after every lane has read it
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
       }
-    if (p.lse != nullptr && h == 0) p.lse[o_row0 + my_q] = kLn2 * (m_ref + log2f(l_sum));
+    } else if (q0 < Sq && my_q < Sq) {
+      uint16_t* orow = p.o + (o_row0 + my_q) * C::DV;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) *(uint2*)(orow + 32 * d + 8 * r4 + 4 * h) = piece(d, r4);
+    }
+    if (p.lse != nullptr && h == 0 && q0 < Sq && my_q < Sq) p.lse[o_row0 + my_q] = kLn2 * (m_ref + log2f(l_sum));
   };
 
   if constexpr (FP8) {
