@@ -11,16 +11,17 @@
 // precision, and the attention kernel can apply the V scale without rounding it
 // into the probabilities.
 //
-// One workgroup of 512 threads per (batch, head, token block); 16 lanes per row, each
-// lane holding chunks of 4 consecutive elements, so that a wave's load covers whole
-// 64-byte runs of 4 rows (whole cache lines); loads and stores carry the nontemporal hint
-// (x is read once, the codes are read by a later kernel). The block stays in registers
-// between the absmax reduction and the conversion, so HBM sees one read of x and one write
-// of the codes; full blocks load without per-row guards, and two or more workgroups share a
-// CU so that one's loads overlap another's arithmetic. There are two kernels, one per head
-// dimension (quantize_d128_kernel, quantize_d192_kernel), each with the rotation as a
-// compile-time option: their lane layouts put the transforms' cross-lane steps on cheap
-// lane exchanges.
+// One workgroup per (batch, head, token block); in the plain passes and the rotation of
+// order 128, 16 lanes per row, each lane holding chunks of 4 consecutive elements, so that
+// a wave's load covers whole 64-byte runs of 4 rows (whole cache lines); loads and stores
+// carry the nontemporal hint (x is read once, the codes are read by a later kernel). The
+// block stays in registers between the absmax reduction and the conversion, so HBM sees one
+// read of x and one write of the codes; full blocks load without per-row guards, and two or
+// more workgroups share a CU so that one's loads overlap another's arithmetic. There are
+// three kernels: quantize_d128_kernel (D = 128, the rotation a compile-time option),
+// quantize_d192_kernel (D = 192, plain) and quantize_d192_rot_kernel (D = 192, rotated, with
+// a lane layout of its own); their lane layouts put the transforms' cross-lane steps on
+// cheap lane exchanges.
 #include <type_traits>
 
 #include "device.h"
@@ -197,20 +198,12 @@ constexpr int paley12(int i, int j) {
   return gf11_chi(j - i);
 }
 
-// One workgroup per (batch, head, token block); 16 lanes per row. Lane l = 4 A + C of a
-// row holds the 3 x 4 elements a = A + 4 k (k < 3), b = 4 C + j (j < 4): three 16-byte
-// chunks, elements 64 k + 16 A + 4 C + j, so that a row's 16 lanes load 256 contiguous bytes
-// per k. H_16 acts on b: bits j in the thread, bits C across lanes l ^ 1, l ^ 2. P_12 acts
-// on a: each lane forms the partial sums of its three a's for all twelve outputs, then a
-// reduce-scatter across lanes l ^ 8 (A ^ 2) and l ^ 4 (A ^ 1) leaves it the full sums for
-// a' = A + 4 k, the positions it loaded. The lane's twelve partial sums are kept in an
-// order of its own (its sign table is permuted to match): positions 0..5 are the outputs
-// it keeps after the exchange with A ^ 2, 0..2 of them the ones it keeps after the exchange
-// with A ^ 1, and positions 6..11 (then 3..5) what its partner keeps, so every exchange
-// sends the same register in both lanes and no value is selected per lane.
+// Plain pass: one workgroup per (batch, head, token block); 16 lanes per row. Lane l = 4 A + C
+// of a row holds the three 16-byte chunks at elements 64 k + 16 A + 4 C (k < 3), so that a
+// row's 16 lanes load 256 contiguous bytes per k.
 constexpr int kR192Threads = 512;  // 32 rows at a time: 4 (or 2) rows per thread; two workgroups fit a CU
 
-template <int BLOCK, bool BF16IN, bool HAD>
+template <int BLOCK, bool BF16IN>
 __global__ __launch_bounds__(kR192Threads) void quantize_d192_kernel(const void* __restrict__ x,
                                                                   uint8_t* __restrict__ codes,
                                                                   float* __restrict__ scales, int S, int nb) {
@@ -256,63 +249,6 @@ __global__ __launch_bounds__(kR192Threads) void quantize_d192_kernel(const void*
     for (int i = 0; i < NR; ++i) load(i, (tid >> 4) + i * (kR192Threads / 16) < ntok);
   }
 
-  constexpr float kNorm = HAD ? 0.07216878364870323f : 1.0f;  // 1/sqrt(192)
-  if constexpr (HAD) {
-    // this lane's Paley signs P[A + 4 k][col(A, u)], in the lane's order of outputs: col(A, u)
-    // = A + 4 u for u < 3, (A ^ 1) + 4 (u - 3) for u < 6 (kept after the A ^ 2 exchange), and
-    // col(A ^ 2, u - 6) for u >= 6 (the partial sums sent to lane A ^ 2)
-    float sgn[3][12];
-#pragma unroll
-    for (int k = 0; k < 3; ++k)
-#pragma unroll
-      for (int u = 0; u < 12; ++u) {
-        auto sign_for = [&](int a) {  // compile-time signs of lane group a
-          const int aa = u < 6 ? a : a ^ 2, uu = u < 6 ? u : u - 6;
-          const int col = uu < 3 ? aa + 4 * uu : (aa ^ 1) + 4 * (uu - 3);
-          return paley12(a + 4 * k, col);
-        };
-        const int s0 = sign_for(0), s1 = sign_for(1), s2 = sign_for(2), s3 = sign_for(3);
-        sgn[k][u] = (float)(A == 0 ? s0 : A == 1 ? s1 : A == 2 ? s2 : s3);
-      }
-    const float sc1 = (C & 1) ? -1.0f : 1.0f, sc2 = (C & 2) ? -1.0f : 1.0f;  // H_16 signs across lanes
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      // H_16 over b = 4 C + j: stages on j inside the thread, on C across lanes
-#pragma unroll
-      for (int k = 0; k < 3; ++k)
-#pragma unroll
-        for (int s = 1; s < 4; s <<= 1)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (!(j & s)) {
-              const float a = v[i][k][j], b = v[i][k][j + s];
-              v[i][k][j] = a + b;
-              v[i][k][j + s] = a - b;
-            }
-#pragma unroll
-      for (int k = 0; k < 3; ++k)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[i][k][j] = fmaf(sc1, v[i][k][j], lane_xor<1>(v[i][k][j]));
-#pragma unroll
-      for (int k = 0; k < 3; ++k)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[i][k][j] = fmaf(sc2, v[i][k][j], lane_xor<2>(v[i][k][j]));
-      // P_12 over a = A + 4 k, for each b
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float part[12];
-#pragma unroll
-        for (int u = 0; u < 12; ++u)
-          part[u] = fmaf(v[i][0][j], sgn[0][u], fmaf(v[i][1][j], sgn[1][u], v[i][2][j] * sgn[2][u]));
-        // lane A ^ 2 sends its positions 6..11: its partial sums of this lane's positions 0..5
-#pragma unroll
-        for (int u = 0; u < 6; ++u) part[u] += lane_xor<8>(part[6 + u]);
-        // lane A ^ 1 sends its positions 3..5: its partial sums of this lane's 0..2
-#pragma unroll
-        for (int u = 0; u < 3; ++u) v[i][u][j] = part[u] + lane_xor_swizzle<4>(part[3 + u]);
-      }
-    }
-  }
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < NR; ++i)
@@ -321,12 +257,10 @@ __global__ __launch_bounds__(kR192Threads) void quantize_d192_kernel(const void*
 #pragma unroll
       for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(v[i][k][j]));
 
-  // block absmax and the power-of-two scale of the values times 1/sqrt(192) (rotated) or
-  // of the values; the final product applies (1/sqrt(192)) 2^-ks at once, which rounds as
-  // the two products would (2^-ks is an exact shift), and stays within +-448
-  const int ks = block_scale_exponent<kR192Threads>(amax * kNorm, red);
+  // block absmax and its power-of-two scale; the product with 2^-ks is an exact shift
+  const int ks = block_scale_exponent<kR192Threads>(amax, red);
   if (tid == 0) scales[blockIdx.x] = ldexpf(1.0f, ks);
-  const float f = ldexpf(kNorm, -ks);
+  const float f = ldexpf(1.0f, -ks);
 
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
@@ -343,12 +277,168 @@ __global__ __launch_bounds__(kR192Threads) void quantize_d192_kernel(const void*
   }
 }
 
+// Rotated pass: four lanes per row. Lane C (< 4) of a row holds b = 4 C + j (j < 4) of all
+// twelve a: the twelve 16-byte chunks at elements 16 a + 4 C. H_16 then has its stages on j
+// inside the thread and its stages on C on DPP quad exchanges, and P_12 runs inside the
+// thread with compile-time signs, in the short form that Paley's construction allows: with
+// X[f] = x[f + 1] (f < 11, read as an element of GF(11)), T the sum of the X and U = x[0] - T,
+//   y[0] = U,   y[f' + 1] = U + 2 (X[f'] + sum over the quadratic residues d of X[f' - d]),
+// since the core's sum of chi(f' - f) X[f] is twice the residue sum minus (T - X[f']), and
+// the diagonal and the first row add X[f'] and x[0]. With the residues {1, 3, 4, 5, 9} the
+// six-term sums share the pairs p[f] = X[f] + X[f - 1] and the triples p[f] + X[f - 2]: 66
+// additions for the twelve outputs where the sign-by-sign form takes 132. A lane's load
+// covers 64 bytes of each of 16 rows, half of a 128-byte line, and the line's other half
+// comes with the next chunk's load: these loads carry no nontemporal hint, with which the
+// pass took about 5 % longer. The codes go out through LDS (below) in 64-byte row runs.
+// Against the sign-by-sign form on the 16-lanes-a-row layout (36 multiply-adds with lane
+// signs and 9 exchanges per column of a lane), the pass runs about 4 % slower at settled
+// clocks and 10 % faster just after the GPU has been idle, when that form's arithmetic
+// made it a fifth slower than the plain pass.
+constexpr int kResidues[5] = {1, 3, 4, 5, 9};
+
+// The short form on integer inputs, checked against P_12 on every unit vector at compile time.
+constexpr bool paley12_short_form_holds() {
+  for (int d : kResidues)
+    if (gf11_chi(d) != 1) return false;
+  for (int a = 0; a < 12; ++a) {
+    int x[12] = {};
+    x[a] = 1;
+    int T = 0;
+    for (int f = 0; f < 11; ++f) T += x[f + 1];
+    const int U = x[0] - T;
+    for (int o = 0; o < 12; ++o) {
+      int y = U;
+      if (o > 0) {
+        const int fo = o - 1;
+        const int p0 = x[1 + fo] + x[1 + (fo + 10) % 11];                                  // d = 0, 1
+        const int t3 = x[1 + (fo + 8) % 11] + x[1 + (fo + 7) % 11] + x[1 + (fo + 6) % 11];  // d = 3, 4, 5
+        y += 2 * (p0 + t3 + x[1 + (fo + 2) % 11]);                                          // d = 9
+      }
+      if (y != paley12(a, o)) return false;
+    }
+  }
+  return true;
+}
+static_assert(paley12_short_form_holds(), "P_12 short form");
+
+template <int BLOCK, bool BF16IN>
+__global__ __launch_bounds__(4 * BLOCK) void quantize_d192_rot_kernel(const void* __restrict__ x,
+                                                                    uint8_t* __restrict__ codes,
+                                                                    float* __restrict__ scales, int S, int nb) {
+  constexpr int D = 192, kThreads = 4 * BLOCK;
+  __shared__ float red[kThreads / 64];
+  const int tid = threadIdx.x, C = tid & 3, row = tid >> 2;
+  const int bh = blockIdx.x / nb;
+  const int blk = blockIdx.x - bh * nb;
+  const int t0 = blk * BLOCK;
+  const int ntok = min(BLOCK, S - t0);
+  const bool live = ntok == BLOCK || row < ntok;
+  const size_t off = ((size_t)bh * S + t0 + row) * D + 4 * C;  // this lane's first chunk
+
+  float v[12][4];
+#pragma unroll
+  for (int a = 0; a < 12; ++a) {
+    if (!live) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[a][j] = 0.0f;
+    } else if constexpr (BF16IN) {
+      typedef unsigned v2u __attribute__((ext_vector_type(2)));
+      const v2u w = *(const v2u*)((const uint16_t*)x + off + 16 * a);
+      v[a][0] = __builtin_bit_cast(float, w[0] << 16);
+      v[a][1] = __builtin_bit_cast(float, w[0] & 0xFFFF0000u);
+      v[a][2] = __builtin_bit_cast(float, w[1] << 16);
+      v[a][3] = __builtin_bit_cast(float, w[1] & 0xFFFF0000u);
+    } else {
+      const v4f w = *(const v4f*)((const float*)x + off + 16 * a);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[a][j] = w[j];
+    }
+  }
+
+  // H_16 over b = 4 C + j: stages on j inside the thread, on C across lanes
+#pragma unroll
+  for (int a = 0; a < 12; ++a)
+#pragma unroll
+    for (int s = 1; s < 4; s <<= 1)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (!(j & s)) {
+          const float lo = v[a][j], hi = v[a][j + s];
+          v[a][j] = lo + hi;
+          v[a][j + s] = lo - hi;
+        }
+  const float sc1 = (C & 1) ? -1.0f : 1.0f, sc2 = (C & 2) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int a = 0; a < 12; ++a)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[a][j] = fmaf(sc1, v[a][j], lane_xor<1>(v[a][j]));
+#pragma unroll
+  for (int a = 0; a < 12; ++a)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[a][j] = fmaf(sc2, v[a][j], lane_xor<2>(v[a][j]));
+
+  // P_12 over a, for each b, in the short form
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float X[11], p[11], t[11];
+#pragma unroll
+    for (int f = 0; f < 11; ++f) X[f] = v[f + 1][j];
+    const float T = ((X[0] + X[1]) + (X[2] + X[3])) + ((X[4] + X[5]) + (X[6] + X[7])) + ((X[8] + X[9]) + X[10]);
+    const float U = v[0][j] - T;
+#pragma unroll
+    for (int f = 0; f < 11; ++f) p[f] = X[f] + X[(f + 10) % 11];
+#pragma unroll
+    for (int f = 0; f < 11; ++f) t[f] = p[f] + X[(f + 9) % 11];
+    v[0][j] = U;
+#pragma unroll
+    for (int f = 0; f < 11; ++f) v[f + 1][j] = fmaf(2.0f, (p[f] + t[(f + 8) % 11]) + X[(f + 2) % 11], U);
+  }
+
+  float amax = 0.0f;
+#pragma unroll
+  for (int a = 0; a < 12; ++a)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(v[a][j]));
+
+  // block absmax and the power-of-two scale of the values times 1/sqrt(192); the final
+  // product applies (1/sqrt(192)) 2^-ks at once, which rounds as the two products would
+  // (2^-ks is an exact shift), and stays within +-448
+  constexpr float kNorm = 0.07216878364870323f;  // 1/sqrt(192)
+  const int ks = block_scale_exponent<kThreads>(amax * kNorm, red);
+  if (tid == 0) scales[blockIdx.x] = ldexpf(1.0f, ks);
+  const float f = ldexpf(kNorm, -ks);
+  // The codes go through the wave's rows of LDS: lane C writes its 4 bytes of each a (bytes
+  // 16 a + 4 C of the row), then reads bytes 64 m + 16 C (m < 3), so that a row's four lanes
+  // store 64 contiguous bytes per instruction rather than four 4-byte pieces 16 bytes apart.
+  // Rows are kRowWords = 52 words apart: 16-byte aligned reads, and the writes of a wave's 16
+  // rows spread over all 32 banks. A row is written and read by its own four lanes only.
+  constexpr int kRowWords = 52;
+  __shared__ unsigned stage[BLOCK * kRowWords];
+  unsigned* const srow = stage + row * kRowWords;
+#pragma unroll
+  for (int a = 0; a < 12; ++a)
+    srow[4 * a + C] = cvt_pk_fp8<true>(v[a][2] * f, v[a][3] * f, cvt_pk_fp8<false>(v[a][0] * f, v[a][1] * f, 0));
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (live) {
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const size_t out = off - 4 * C;  // the row's first code
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+      __builtin_nontemporal_store(*(const v4u*)(srow + 16 * m + 4 * C), (v4u*)(codes + out + 64 * m + 16 * C));
+  }
+}
+
 template <int D, int BLOCK, bool BF16IN, bool HAD>
 static hipError_t launch_q(const QuantArgs& a, hipStream_t stream) {
   const int nb = (a.S + BLOCK - 1) / BLOCK;
   const long long grid = (long long)a.B * a.H * nb;
-  if constexpr (D == 192) {
-    hipLaunchKernelGGL((quantize_d192_kernel<BLOCK, BF16IN, HAD>), dim3((unsigned)grid), dim3(kR192Threads), 0, stream,
+  if constexpr (D == 192 && HAD) {
+    hipLaunchKernelGGL((quantize_d192_rot_kernel<BLOCK, BF16IN>), dim3((unsigned)grid), dim3(4 * BLOCK), 0, stream,
+                       a.x, a.codes, a.scales, a.S, nb);
+  } else if constexpr (D == 192) {
+    hipLaunchKernelGGL((quantize_d192_kernel<BLOCK, BF16IN>), dim3((unsigned)grid), dim3(kR192Threads), 0, stream,
                        a.x, a.codes, a.scales, a.S, nb);
   } else {
     hipLaunchKernelGGL((quantize_d128_kernel<BLOCK, BF16IN, HAD>), dim3((unsigned)grid), dim3(kR128Threads), 0, stream,
