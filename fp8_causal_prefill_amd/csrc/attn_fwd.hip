@@ -340,9 +340,14 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
   // whole tiles), and the row of the cache ([pages x Hkv x page rows] rows of D) holding
   // the tile's first key. Page indices are clamped to the table and the cache, so a
   // malformed table reads wrong rows, never past the tensors.
+  // (the table is read through the constant address space: nothing writes it while the
+  // kernel runs, so the entry comes in by a scalar load. A vector load of the one address
+  // made every wave wait, at each iteration, for its earlier tile copies as well: the
+  // vector memory counter drains in order, and the entry is needed in a scalar register.)
   auto page_of = [&](int t) -> int {
     const int j = min((k_begin + t * C::BN) >> p.page_shift, p.max_pages - 1);
-    return min(max(p.block_table[(size_t)b * p.max_pages + j], 0), p.num_pages - 1);
+    const auto table = (const __attribute__((address_space(4))) int*)p.block_table;
+    return min(max(table[(size_t)b * p.max_pages + j], 0), p.num_pages - 1);
   };
   auto page_row = [&](int pg, int t) -> size_t {
     return (((size_t)pg * p.Hkv + hkv) << p.page_shift) + ((k_begin + t * C::BN) & ((1 << p.page_shift) - 1));
