@@ -334,24 +334,55 @@ __global__ __launch_bounds__(4 * BLOCK) void quantize_d192_rot_kernel(const void
   const int ntok = min(BLOCK, S - t0);
   const bool live = ntok == BLOCK || row < ntok;
   const size_t off = ((size_t)bh * S + t0 + row) * D + 4 * C;  // this lane's first chunk
+  typedef unsigned v2u __attribute__((ext_vector_type(2)));
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  // The workgroup's rows in LDS, kRowWords words apart: the codes on their way out and,
+  // with bfloat16 input, the input on its way in. A wave uses only its own 16 rows, so
+  // ordering within the wave is all the staging needs.
+  constexpr int kRowWords = BF16IN ? 104 : 52;
+  __shared__ unsigned rows_lds[BLOCK * kRowWords];
+  unsigned* const srow = rows_lds + row * kRowWords;
 
   float v[12][4];
+  if constexpr (BF16IN) {
+    // A bfloat16 chunk is 8 bytes, so loads in the lane layout would cover 32 bytes of each
+    // of 16 rows. A wave's 16 rows are 6 KiB of contiguous input instead: six loads of 16
+    // bytes a lane, each a contiguous KiB, go to the wave's LDS rows (104 words apart: 16-byte
+    // aligned, and the 8-byte reads below take the four passes their 512 bytes need), and
+    // each lane reads its chunks from there. Rows past the tensor's end hold zeros.
+    const int wrow0 = (tid >> 6) * 16, l = tid & 63;
+    const char* const src = (const char*)x + ((size_t)bh * S + t0 + wrow0) * (2 * D);
+    char* const dst = (char*)(rows_lds + wrow0 * kRowWords);
 #pragma unroll
-  for (int a = 0; a < 12; ++a) {
-    if (!live) {
+    for (int i = 0; i < 6; ++i) {
+      const int byte = 1024 * i + 16 * l;  // within the wave's 6 KiB
+      const int rr = byte / (2 * D), cc = byte - rr * (2 * D);
+      v4u w = v4u{0u, 0u, 0u, 0u};
+      if (ntok == BLOCK || wrow0 + rr < ntok) w = *(const v4u*)(src + byte);
+      *(v4u*)(dst + rr * (4 * kRowWords) + cc) = w;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[a][j] = 0.0f;
-    } else if constexpr (BF16IN) {
-      typedef unsigned v2u __attribute__((ext_vector_type(2)));
-      const v2u w = *(const v2u*)((const uint16_t*)x + off + 16 * a);
+    for (int a = 0; a < 12; ++a) {
+      const v2u w = *(const v2u*)((const char*)srow + 32 * a + 8 * C);
       v[a][0] = __builtin_bit_cast(float, w[0] << 16);
       v[a][1] = __builtin_bit_cast(float, w[0] & 0xFFFF0000u);
       v[a][2] = __builtin_bit_cast(float, w[1] << 16);
       v[a][3] = __builtin_bit_cast(float, w[1] & 0xFFFF0000u);
-    } else {
-      const v4f w = *(const v4f*)((const float*)x + off + 16 * a);
+    }
+  } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[a][j] = w[j];
+    for (int a = 0; a < 12; ++a) {
+      if (!live) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[a][j] = 0.0f;
+      } else {
+        const v4f w = *(const v4f*)((const float*)x + off + 16 * a);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[a][j] = w[j];
+      }
     }
   }
 
@@ -407,14 +438,12 @@ __global__ __launch_bounds__(4 * BLOCK) void quantize_d192_rot_kernel(const void
   const int ks = block_scale_exponent<kThreads>(amax * kNorm, red);
   if (tid == 0) scales[blockIdx.x] = ldexpf(1.0f, ks);
   const float f = ldexpf(kNorm, -ks);
-  // The codes go through the wave's rows of LDS: lane C writes its 4 bytes of each a (bytes
+  // The codes go through the row's LDS words: lane C writes its 4 bytes of each a (bytes
   // 16 a + 4 C of the row), then reads bytes 64 m + 16 C (m < 3), so that a row's four lanes
   // store 64 contiguous bytes per instruction rather than four 4-byte pieces 16 bytes apart.
-  // Rows are kRowWords = 52 words apart: 16-byte aligned reads, and the writes of a wave's 16
-  // rows spread over all 32 banks. A row is written and read by its own four lanes only.
-  constexpr int kRowWords = 52;
-  __shared__ unsigned stage[BLOCK * kRowWords];
-  unsigned* const srow = stage + row * kRowWords;
+  // (52 words apart, the writes of a wave's 16 rows spread over all 32 banks.) A row is
+  // written and read by its own four lanes only; with bfloat16 input its input words were
+  // all read before: a wave's LDS operations complete in order.
 #pragma unroll
   for (int a = 0; a < 12; ++a)
     srow[4 * a + C] = cvt_pk_fp8<true>(v[a][2] * f, v[a][3] * f, cvt_pk_fp8<false>(v[a][0] * f, v[a][1] * f, 0));
@@ -422,7 +451,6 @@ __global__ __launch_bounds__(4 * BLOCK) void quantize_d192_rot_kernel(const void
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   if (live) {
-    typedef unsigned v4u __attribute__((ext_vector_type(4)));
     const size_t out = off - 4 * C;  // the row's first code
 #pragma unroll
     for (int m = 0; m < 3; ++m)
