@@ -83,21 +83,23 @@ def test_quantize_hadamard(S, block, D):
     assert mismatch < 1e-3, mismatch
 
 
-@pytest.mark.parametrize("D", [128, 192])
-def test_quantize_hadamard_bf16_input(D):
+@pytest.mark.parametrize("D,block,S", [(128, 64, 200), (192, 64, 200), (128, 128, 333), (192, 128, 333),
+                                       (192, 128, 17)])
+def test_quantize_hadamard_bf16_input(D, block, S):
     # the bfloat16-input rotation paths (D = 128: the fast Walsh-Hadamard transform; D = 192:
-    # the Paley-Sylvester product): every code a nearest e4m3 value of the exact rotation of
-    # the bfloat16 values the kernel read, divided by the block's power-of-two scale
-    _print_case(D=D, bf16=True)
-    w = custom(1, 3, 3, 200, D, 128, dist="activation", wid=470 + D)
+    # the Paley-Sylvester product, whose bfloat16 rows come in through LDS): every code a
+    # nearest e4m3 value of the exact rotation of the bfloat16 values the kernel read, divided
+    # by the block's power-of-two scale; ragged last blocks (8, 77 and 17 rows of a block)
+    _print_case(D=D, block=block, S=S, bf16=True)
+    w = custom(1, 3, 3, S, D, 128, dist="activation", wid=470 + D + S)
     x, _, _ = generate(w, seed=5)
     xb = torch.from_numpy(x).to(torch.bfloat16)
-    codes, scales = zy.quantize_fp8(xb.to("cuda"), 64, True)
+    codes, scales = zy.quantize_fp8(xb.to("cuda"), block, True)
     codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
     y = hadamard_rotate(xb.float().numpy())  # the bf16 values the kernel read, rotated exactly
     m, _ = np.frexp(scales.astype(np.float64))
     assert np.all(m == 0.5)
-    s = np.repeat(scales.astype(np.float64), 64, axis=2)[:, :, :200, None]
+    s = np.repeat(scales.astype(np.float64), block, axis=2)[:, :, :S, None]
     t = y / s
     err = np.abs(e4m3_decode(codes) - t)
     half_ulp = np.maximum(np.abs(t) * 2.0 ** -4, 2.0 ** -10)
@@ -105,5 +107,5 @@ def test_quantize_hadamard_bf16_input(D):
     # the scale is the least power of two that holds the block's rotated absmax (up to the
     # float32 rotation's noise at a binade boundary)
     for j in range(scales.shape[2]):
-        r = np.abs(y[:, :, 64 * j:64 * (j + 1)]).max(axis=(2, 3)) / scales[:, :, j]
+        r = np.abs(y[:, :, block * j:block * (j + 1)]).max(axis=(2, 3)) / scales[:, :, j]
         assert np.all(r <= 448 * (1 + 1e-6)) and np.all(r > 224 * (1 - 1e-6))
