@@ -286,10 +286,11 @@ __global__ __launch_bounds__(kR192Threads) void quantize_d192_kernel(const void*
 // since the core's sum of chi(f' - f) X[f] is twice the residue sum minus (T - X[f']), and
 // the diagonal and the first row add X[f'] and x[0]. With the residues {1, 3, 4, 5, 9} the
 // six-term sums share the pairs p[f] = X[f] + X[f - 1] and the triples p[f] + X[f - 2]: 66
-// additions for the twelve outputs where the sign-by-sign form takes 132. A lane's load
-// covers 64 bytes of each of 16 rows, half of a 128-byte line, and the line's other half
-// comes with the next chunk's load: these loads carry no nontemporal hint, with which the
-// pass took about 5 % longer. The codes go out through LDS (below) in 64-byte row runs.
+// additions for the twelve outputs where the sign-by-sign form takes 132. With float32
+// input a lane's load covers 64 bytes of each of 16 rows, half of a 128-byte line, and the
+// line's other half comes with the next chunk's load: these loads carry no nontemporal hint,
+// with which the pass took about 5 % longer. Bfloat16 rows come in through LDS (below), and
+// the codes go out through LDS in 64-byte row runs.
 // Against the sign-by-sign form on the 16-lanes-a-row layout (36 multiply-adds with lane
 // signs and 9 exchanges per column of a lane), the pass runs about 4 % slower at settled
 // clocks and 10 % faster just after the GPU has been idle, when that form's arithmetic
