@@ -9,7 +9,13 @@ lean 3e-2, BF16 5e-3; log-sum-exp within ln(1 + 2^-4), 0.1 and 1e-3). A case who
 that see a key number fewer than 64 is held to twice the bar: an L2 error over a handful
 of rows is a small sample of the per-row error, whose spread the bars do not cover.
 Rows that see no key must hold exactly 0 with LSE = -inf; rows of no sequence must keep
-the sentinel the test wrote."""
+the sentinel the test wrote.
+
+The quantizer's cases (head dimension, scale block, length, input type, rotation, value
+distribution and magnitude drawn per case) are held to the quantizer tests' bars: without
+rotation codes and scales equal the oracle's bit for bit; with it every code is a correct
+rounding of the exactly rotated value over the kernel's scale, and every scale the least
+power of two that holds its block's rotated absmax."""
 
 import math
 
@@ -18,7 +24,8 @@ import pytest
 import torch
 
 import fp8_causal_prefill_amd as zy
-from oracle import dequantize_blocks, paged_attention, varlen_attention, window_attention
+from oracle import (dequantize_blocks, e4m3_decode, hadamard_rotate, paged_attention, quantize_blocks,
+                    varlen_attention, window_attention)
 from tests.paths import bf16_from_f64, rel_l2, to_dev
 from tests.test_gpu_decode import Decode
 from tests.test_gpu_paged import Paged
@@ -147,3 +154,36 @@ def test_random_decode(seed):
     og, lg, deq = d.run(mode, block=block, split_keys=split)
     ro, rl = d.oracle(deq, 1 / math.sqrt(Dqk))
     _check(mode, og, lg, ro, rl, len(kv) * Hq)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_quantize(seed):
+    rng = np.random.default_rng([1205, seed])
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 6))
+    D, block = int(rng.choice([128, 192])), int(rng.choice([64, 128]))
+    S = int(rng.integers(1, 700))
+    bf16, had = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    dist = str(rng.choice(["gaussian", "activation"]))
+    mag = 2.0 ** float(rng.uniform(-20, 20))
+    _case(dict(B=B, H=H, D=D, block=block, S=S, bf16=bf16, hadamard=had, dist=dist, magnitude=mag))
+    x, _, _ = generate(custom(B, H, H, S, D, 128, dist=dist, wid=1220 + seed), seed=seed)
+    xt = torch.from_numpy((x * np.float32(mag)).astype(np.float32))
+    if bf16:
+        xt = xt.to(torch.bfloat16)
+    xr = xt.float().numpy()  # the values the kernel reads
+    codes, scales = zy.quantize_fp8(xt.to("cuda"), block, had)
+    codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
+    if not had:
+        rc, rs = quantize_blocks(xr, block)
+        assert np.array_equal(scales, rs) and np.array_equal(codes, rc)
+        return
+    y = hadamard_rotate(xr)  # exact rotation (float64)
+    m, _ = np.frexp(scales.astype(np.float64))
+    assert np.all(m == 0.5)
+    t = y / np.repeat(scales.astype(np.float64), block, axis=2)[:, :, :S, None]
+    err = np.abs(e4m3_decode(codes) - t)
+    half_ulp = np.maximum(np.abs(t) * 2.0 ** -4, 2.0 ** -10)
+    assert np.all(err <= half_ulp * (1 + 1e-5) + np.abs(t) * 1e-6)
+    for j in range(scales.shape[2]):
+        r = np.abs(y[:, :, block * j:block * (j + 1)]).max(axis=(2, 3)) / scales[:, :, j]
+        assert np.all(r <= 448 * (1 + 1e-6)) and np.all(r > 224 * (1 - 1e-6))
