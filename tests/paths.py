@@ -33,6 +33,23 @@ def bf16_from_f64(t: torch.Tensor):
 
 # ---------------- GPU side ----------------
 
+# float32 error of the kernels' rotation, as a multiple of 2^-24 * sum |x| / sqrt(D) over the
+# row: the order-128 transform is 7 butterfly stages and the scaling (at most 9 roundings
+# along any path, each bounded by the sum of the magnitudes it adds); the order-192 product
+# is 4 stages of H_16 and the order-12 sums (at most 8 roundings deep, over terms bounded by
+# three times the row's magnitude sum), about 30. One bound serves both.
+ROTATION_NOISE_ULPS = 32
+
+
+def rotation_noise(x, scales, block):
+    """Per-element bound on |t32 - t| for codes of a rotated x [B, H, S, D] with block scales
+    [B, H, nb]: t is the exact rotated value over its scale, t32 the kernel's float32 one."""
+    S, D = x.shape[2], x.shape[3]
+    row = np.abs(x.astype(np.float64)).sum(axis=-1, keepdims=True)
+    s = np.repeat(scales.astype(np.float64), block, axis=2)[:, :, :S, None]
+    return ROTATION_NOISE_ULPS * 2.0 ** -24 * row / math.sqrt(D) / s
+
+
 def gpu_quantize(x, block, hadamard=False):
     codes, scales = zy.quantize_fp8(to_dev(x), block, hadamard)
     return codes, scales

@@ -15,7 +15,7 @@ import torch
 import fp8_causal_prefill_amd as zy
 from oracle import quantize_blocks, hadamard_rotate, e4m3_decode
 from workloads import custom, generate
-from tests.paths import gpu_quantize, to_dev
+from tests.paths import gpu_quantize, rotation_noise, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -75,10 +75,13 @@ def test_quantize_hadamard(S, block, D):
     # every GPU code decodes to a nearest e4m3 value of y / s up to float32 noise in y
     s = np.repeat(scales.astype(np.float64), block, axis=2)[:, :, :S, None]
     t = y / s
+    noise = rotation_noise(x, scales, block)  # the kernel's float32 rotation error, in code units
     dec = e4m3_decode(codes)
     err = np.abs(dec - t)
     half_ulp = np.maximum(np.abs(t) * 2.0 ** -4, 2.0 ** -10)
-    assert np.all(err <= half_ulp * (1 + 1e-5) + np.abs(t) * 1e-6)
+    # (half a step of the kernel's float32 value t32 is at most half a step of t plus 2^-4 of
+    # |t32 - t|; 2^-20 |t| covers the roundings of the scale product)
+    assert np.all(err <= half_ulp + noise * (1 + 2.0 ** -4) + np.abs(t) * 2.0 ** -20)
     mismatch = np.mean(codes != rc)
     assert mismatch < 1e-3, mismatch
 
@@ -101,9 +104,12 @@ def test_quantize_hadamard_bf16_input(D, block, S):
     assert np.all(m == 0.5)
     s = np.repeat(scales.astype(np.float64), block, axis=2)[:, :, :S, None]
     t = y / s
+    noise = rotation_noise(xb.float().numpy(), scales, block)  # float32 rotation error, in code units
     err = np.abs(e4m3_decode(codes) - t)
     half_ulp = np.maximum(np.abs(t) * 2.0 ** -4, 2.0 ** -10)
-    assert np.all(err <= half_ulp * (1 + 1e-5) + np.abs(t) * 1e-6)
+    # (half a step of the kernel's float32 value t32 is at most half a step of t plus 2^-4 of
+    # |t32 - t|; 2^-20 |t| covers the roundings of the scale product)
+    assert np.all(err <= half_ulp + noise * (1 + 2.0 ** -4) + np.abs(t) * 2.0 ** -20)
     # the scale is the least power of two that holds the block's rotated absmax (up to the
     # float32 rotation's noise at a binade boundary)
     for j in range(scales.shape[2]):
