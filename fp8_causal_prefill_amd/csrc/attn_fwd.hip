@@ -442,6 +442,10 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
     }
   };
   const uint32_t k_lds = lds_address(kring), v_lds = lds_address(vring);
+  // One-wave workgroups serve decode, where every cached key and value tile is read by one
+  // workgroup only: their copies carry the nontemporal hint (8 x 32K keys: 95.5 against
+  // 100.7 us). Prefill tiles are read by every query tile of their head, through L2.
+  constexpr bool kStreamKV = WAVES == 1;
 
   // first K / V byte of key tile t (t0 = t * BN; PAGED: in cache page pg)
   auto k_tile = [&](int t, int pg) -> const char* {
@@ -461,7 +465,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
       for (int i = 0; i < C::KCHUNKS; ++i) {
         uint32_t off;
         const char* base = k_copy(tile, i, off);
-        if (k_live(i)) lds_copy16(base, off, dst + i * C::THREADS * 16);
+        if (k_live(i)) lds_copy16<kStreamKV>(base, off, dst + i * C::THREADS * 16);
       }
     } else {
       // rows past the window's last key repeat it (>= t0: the same tile, and page)
@@ -483,7 +487,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
       for (int i = 0; i < C::VCHUNKS; ++i) {
         uint32_t off;
         const char* base = v_copy(tile, i, off);
-        if (v_live(i)) lds_copy16(base, off, dst + i * C::THREADS * 16);
+        if (v_live(i)) lds_copy16<kStreamKV>(base, off, dst + i * C::THREADS * 16);
       }
     } else {
       const char* tile = PAGED ? v_tile(t, pg) : vbase;
@@ -503,7 +507,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
     for (int i = 0; i < C::KCHUNKS; ++i) {
       uint32_t off;
       const char* base = k_copy(tile, i, off);
-      if (k_live(i)) lds_copy16(base, off, dst + i * C::THREADS * 16);
+      if (k_live(i)) lds_copy16<kStreamKV>(base, off, dst + i * C::THREADS * 16);
     }
   };
   auto fill_v_full = [&](int t, int buf, int pg) {
@@ -513,7 +517,7 @@ __global__ __launch_bounds__((Cfg<FP8, DQK, WAVES>::THREADS), (WAVES == 1 ? 1 : 
     for (int i = 0; i < C::VCHUNKS; ++i) {
       uint32_t off;
       const char* base = v_copy(tile, i, off);
-      if (v_live(i)) lds_copy16(base, off, dst + i * C::THREADS * 16);
+      if (v_live(i)) lds_copy16<kStreamKV>(base, off, dst + i * C::THREADS * 16);
     }
   };
   // make this wave's copies complete before the barrier that publishes them

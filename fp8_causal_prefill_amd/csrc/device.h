@@ -127,14 +127,20 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 // source = base (wave-uniform) + off (per lane, bytes)
+template <bool NT = false>  // NT: the nontemporal hint, for data read once (decode's cache)
 __device__ __forceinline__ void lds_copy16(const void* base, uint32_t off, uint32_t lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const uint64_t b = (uint64_t)(uintptr_t)base;
   const uint64_t bu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(bu),
-               "s"(__builtin_amdgcn_readfirstlane((int)lds))
-               : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(off), "s"(bu),
+                 "s"(__builtin_amdgcn_readfirstlane((int)lds))
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(bu),
+                 "s"(__builtin_amdgcn_readfirstlane((int)lds))
+                 : "memory", "m0");
 #endif
 }
 // source = src (per lane)
