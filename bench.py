@@ -146,24 +146,61 @@ def cpu_baseline(w, q, k, v, target_s=15.0):
 
 def time_kernel(fn, steps, warmup, stream, torch):
     """Mean and median milliseconds of fn() from HIP events on the stream it launches on.
-    Two untimed launches go first, so that the first timed one does not start from an
-    idle queue (the host's time per call would show as GPU time before its kernel)."""
+    Issuing a call from Python (argument checks, two event records) takes the host tens of
+    microseconds. Calls whose kernels run ten times longer or more queue up by themselves
+    after two untimed launches. Shorter ones would leave the GPU waiting for the host, and
+    events recorded as they are issued would time part of the host's work: those calls are
+    queued behind a spin kernel that keeps the stream busy until all of them are issued, so
+    that each event pair brackets its own launch, run back to back with the others. (Longer
+    kernels are not queued that way: a burst of them after the idle spin runs a few percent
+    slower than the same kernels back to back, as the board's power control catches up.)"""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    ev = []
-    fn()
-    fn()
-    for _ in range(steps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    n0 = min(steps, 8)
+    t0 = time.perf_counter()
+    for e0, e1 in ev[:n0]:
         e0.record(stream)
         fn()
         e1.record(stream)
-        ev.append((e0, e1))
+    host_ms = 1e3 * (time.perf_counter() - t0) / n0  # issue time per call (the queue is not full)
+    torch.cuda.synchronize()
+    kernel_ms = min(a.elapsed_time(b) for a, b in ev[:n0])
+    rate = spin_cycles_per_ms(torch) if kernel_ms < 10.0 * host_ms else None
+    if rate is not None:
+        backlog_ms = min(2.0 + 3.0 * host_ms * steps, 300.0)  # margin for a clock faster than at calibration
+        torch.cuda._sleep(int(backlog_ms * rate))
+    else:
+        fn()
+        fn()
+    for e0, e1 in ev:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
     torch.cuda.synchronize()
     ms = [a.elapsed_time(b) for a, b in ev]
     return float(np.mean(ms)), float(np.median(ms))
+
+
+_SPIN_CYCLES_PER_MS = None
+
+
+def spin_cycles_per_ms(torch):
+    """Counter ticks per millisecond of torch's spin kernel on this GPU, measured once
+    (None if the measurement is implausible)."""
+    global _SPIN_CYCLES_PER_MS
+    if _SPIN_CYCLES_PER_MS is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        e0.record()
+        torch.cuda._sleep(2_000_000)
+        e1.record()
+        torch.cuda.synchronize()
+        rate = 2_000_000 / max(e0.elapsed_time(e1), 1e-6)
+        # a counter between 10 MHz and 10 GHz; anything else and the calls go unqueued
+        _SPIN_CYCLES_PER_MS = rate if 1e4 <= rate <= 1e7 else False
+    return _SPIN_CYCLES_PER_MS or None
 
 
 class Telemetry:
