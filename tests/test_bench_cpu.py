@@ -1,5 +1,6 @@
 """bench.py's host logic, without a GPU: the one-GPU guard, the traffic record's source
-hash check, the CPU description of the baseline and the summary of timeline records."""
+hash check (and that the committed records match the kernel source), the CPU description
+of the baseline, the summary of timeline records and the choice of how a kernel is timed."""
 
 import json
 import os
@@ -66,3 +67,55 @@ def test_timeline_summary_of_synthetic_records():
     assert s2["workgroups"] == 4 and abs(s2["gap_us_mean"] - 1.5) < 1e-9
     assert s2["xcd_end_us"] == [22.0, 21.0]
     assert abs(s2["prologue_us_mean"] - 1.0) < 1e-9
+
+
+def test_traffic_records_were_taken_on_the_current_kernel_source():
+    # the bench line's roofline.traffic comes from these records; a kernel change needs them retaken
+    for dtype in ("fp8", "fp8_lean", "bf16"):
+        rec = json.load(open(os.path.join(ROOT, "profiles", f"attn_fwd_{dtype}_gqa32k_hbm.json")))
+        assert rec["kernel_source_hash"] == bench.kernel_hash(), dtype
+
+
+class _FakeClock:
+    """A stand-in for torch.cuda's events and spin kernel: each call of fn advances a GPU
+    timeline by its kernel time; the host issue time is simulated by the test."""
+
+    def __init__(self, kernel_ms):
+        self.kernel_ms, self.gpu_ms, self.sleeps = kernel_ms, 0.0, []
+        outer = self
+
+        class Event:
+            def __init__(self, enable_timing=False):
+                self.t = None
+
+            def record(self, stream=None):
+                self.t = outer.gpu_ms
+
+            def elapsed_time(self, other):
+                return other.t - self.t
+
+        class Cuda:
+            pass
+
+        self.cuda = Cuda()
+        self.cuda.Event = Event
+        self.cuda.synchronize = lambda: None
+        self.cuda._sleep = lambda cycles: self.sleeps.append(cycles)
+
+    host_s = 0.0
+
+    def fn(self):  # each call takes the host 50 us to issue
+        self.gpu_ms += self.kernel_ms
+        _FakeClock.host_s += 50e-6
+
+
+def test_short_kernels_are_queued_behind_a_spin_and_long_ones_are_not(monkeypatch):
+    monkeypatch.setattr(bench, "spin_cycles_per_ms", lambda torch: 2.0e6)
+    monkeypatch.setattr(bench.time, "perf_counter", lambda: _FakeClock.host_s)
+    for kernel_ms, spins in ((0.1, True), (1.2, False)):
+        fake = _FakeClock(kernel_ms)
+        mean, median = bench.time_kernel(fake.fn, 20, 3, None, fake)
+        assert abs(mean - kernel_ms) < 1e-9 and abs(median - kernel_ms) < 1e-9
+        assert bool(fake.sleeps) == spins
+        if spins:  # long enough for the issue of every timed call, and bounded
+            assert 2.0e6 * (20 * 0.05) <= fake.sleeps[0] <= 2.0e6 * 300
