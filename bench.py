@@ -16,7 +16,9 @@ reported in ``fp8_lean`` and BF16 in ``bf16``; ``range`` times the range entry p
 (chunked prefill, split-KV with the merge kernel and its HBM roofline) and ``varlen`` a
 packed batch of eight sequences of 256 to 16384 tokens on the same tensors. The CPU baseline times the fp64 oracle
 on a bounded sample (whole query heads, about 15 s) on the host cores; the heads it
-computed also give a full-size parity figure (``sampled_rel_l2_fp8``).
+computed also give a full-size parity figure (``sampled_rel_l2_fp8``). ``cold_caches``
+times the FP8 kernel again, each launch after a 512 MiB fill that evicts its inputs from
+L2 and the Infinity Cache (median and mean of twice ``--steps`` launches).
 
 ``sustained`` runs each headline kernel back to back for a few seconds after the clock
 has settled and reports, next to its time, the median shader clock, the socket power,
@@ -879,6 +881,8 @@ def main():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-lean", action="store_true", help="skip the lean-probability FP8 mode")
     ap.add_argument("--no-others", action="store_true", help="skip the other workload shapes")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the FP8 kernel timed after flushes of L2 and the Infinity Cache")
     ap.add_argument("--no-range", action="store_true", help="skip the varlen, chunked-prefill, split-KV, paged and decode measurements")
     ap.add_argument("--sustain", type=float, default=4.0,
                     help="seconds of back-to-back launches per headline kernel, after 1.5 s of settling, "
@@ -1076,6 +1080,28 @@ def main():
             if not args.no_others:
                 sustained_rec["structured_inputs"] = structured_sustained(tel, args.sustain, stream, torch, zy)
 
+    # ---------------- cold caches: the FP8 kernel after each flush of L2 and the Infinity Cache ----------------
+    cold = None
+    if not args.no_cold:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)  # twice the 256 MiB Infinity Cache
+        evc = []
+        for i in range(2 * args.steps + 2):
+            flush.fill_(i & 0xFF)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            zy.attn_fwd_fp8(qc, kc, vc, qs, ks, vs, blk, scale, o=o8)
+            e1.record(stream)
+            if i >= 2:
+                evc.append((e0, e1))
+        torch.cuda.synchronize()
+        cms = [a.elapsed_time(b) for a, b in evc]
+        cold = {"launches": len(cms), "flush_bytes": 512 << 20, "ms_median": float(np.median(cms)),
+                "ms_mean": float(np.mean(cms)), "warm_ms_median": attn_med_s * 1e3}
+        del flush
+        print(f"[bench] fp8 attention after cache flushes: median {cold['ms_median']:.3f} ms over {len(cms)} launches",
+              file=sys.stderr, flush=True)
+
     achieved = flops / attn_s / 1e12
     line = {
         "metric": "causal prefill attn TFLOPS + % of FP8 MFMA peak, S=32K D=128 (FP8 & BF16)",
@@ -1101,6 +1127,7 @@ def main():
         "fp8_lean": lean,
         "bf16": bf16,
         "sustained": sustained_rec,
+        "cold_caches": cold,
     }
 
     if not args.no_range:
