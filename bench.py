@@ -734,12 +734,51 @@ def decode_batch(w, kc, vc, ks, vs, kd, vd, steps, warmup, stream, torch, zy):
     total = kv_bytes + part_bytes + B * w.Hq * (w.Dqk + 2 * w.Dv)
     print(f"[bench] decode B={B} x {S} keys: {ms * 1e3:.1f} us ({total / ms / 1e6:.0f} GB/s)", file=sys.stderr,
           flush=True)
+    # The same call captured in a HIP graph and replayed back to back (Inference Wave 2,
+    # "Methodology and Limitations": kernel timings under graph capture and replay). The
+    # allocation-free entry point is the one a capturing caller uses: its splits' partial
+    # results go to the library's scratch array.
+    o_eager = o.clone()
+    try:
+        def call():
+            zy.attn_decode_fp8_paged_noalloc(qc, kp, vp, qs, ksp, vsp, blk, kvl, bt, S, o,
+                                             softmax_scale=w.softmax_scale, split_keys=split)
+
+        call()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gms = e0.elapsed_time(e1) / steps
+        graph = {"entry_point": "zyfa_attn_decode_fp8_paged_noalloc", "replays": steps, "ms": gms,
+                 "output_equals_eager_call": bool(torch.equal(o, o_eager)),
+                 "achieved_gbs": total / gms / 1e6, "frac_of_hbm": total / gms / 1e6 / PEAK_HBM_GBS}
+        print(f"[bench] decode as graph replays: {gms * 1e3:.1f} us ({total / gms / 1e6:.0f} GB/s)", file=sys.stderr,
+              flush=True)
+        del g
+    except Exception as e:  # recorded, not fatal: the eager figures above stand
+        graph = {"error": repr(e)}
     del kp, vp, ksp, vsp, qc
     rec = {"batch": B, "kv_len": S, "heads": f"Hq={w.Hq} Hkv={w.Hkv} D={w.Dqk}", "page_size": PAGE_SIZE,
            "split_keys": split, "n_splits": n_splits, "ms": ms, "ms_median": med,
            "roofline": {"bound": "hbm", "achieved": total / ms / 1e6, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": total / ms / 1e6 / PEAK_HBM_GBS, "bytes_per_call": total,
-                        "kv_bytes": kv_bytes}}
+                        "kv_bytes": kv_bytes},
+           "graph": graph}
     # BF16: the same batch in bfloat16 (twice the cache bytes, no scales)
     qb, _, kpb, vpb, _, _, kvl, bt = decode_setup(w, kd.to(torch.bfloat16), vd.to(torch.bfloat16), None, None,
                                                    torch, zy)
